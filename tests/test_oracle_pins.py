@@ -1,0 +1,417 @@
+"""Pins of the fp64 oracle to facts other than itself.
+
+The TokenSpeed pages print no value of the GDN state update, so the oracle is
+pinned by what the gated delta rule fixes mathematically: a worked example
+derived by hand, closed forms, invariants, a complete characterisation of the
+rank-one delta write, the agreement of two different algorithms (token loop and
+chunk form), and the slot semantics. Each pin is chosen so that a plausible
+slip in the oracle (a dropped decay, a wrong sign, a transposed state, output
+read before the write, a wrong head map, a misplaced scale) fails at least one.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import (
+    GDN_E_ALIAS,
+    GDN_E_INVALID,
+    GDN_E_NO_SLOTS,
+    GDN_E_SLOT_STATE,
+    GDN_OK,
+    SlotPoolModel,
+    bf16_bits_to_f64,
+    chunked_sequence,
+    decode_step,
+    l2_normalize,
+    prefill,
+    recurrent_sequence,
+)
+from hybrid_linear_attention_02_amd.workloads import f32_to_bf16_bits
+
+
+def _unit(rng, *shape):
+    x = rng.standard_normal(shape)
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _nrm_err(x, y):
+    return np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-300)
+
+
+# ---------------------------------------------------------------------------
+# worked example, derived by hand
+# ---------------------------------------------------------------------------
+
+def test_hand_worked_two_tokens():
+    """dk = dv = 2, one head, scale 1, eps 0. Derivation (S is dv x dk):
+
+    S0 = [[1, 2], [3, 4]].
+    token 1: k = (3, 4) -> k^ = (0.6, 0.8); q = (0, 5) -> q~ = (0, 1);
+      exp(g) = 1/2, beta = 1/2, v = (1, -1).
+      decay:  S = [[0.5, 1], [1.5, 2]];  S k^ = (1.1, 2.5)
+      beta (v - S k^) = (-0.05, -1.75);  outer with k^ = [[-0.03, -0.04], [-1.05, -1.4]]
+      S1 = [[0.47, 0.96], [0.45, 0.6]];  o1 = S1 q~ = (0.96, 0.6)
+    token 2: k = (1, 0); q = (1, 1) -> q~ = (1, 1)/sqrt(2); g = 0; beta = 1;
+      v = (2, 3).  S k^ = (0.47, 0.45); v - S k^ = (1.53, 2.55)
+      S2 = [[2, 0.96], [3, 0.6]];  o2 = (2.96, 3.6)/sqrt(2)
+    Storage holds H = S^T.
+    """
+    H0 = np.array([[[1.0, 3.0], [2.0, 4.0]]])                 # [HV=1, dk, dv] = S0^T
+    q = np.array([[[0.0, 5.0]], [[1.0, 1.0]]])
+    k = np.array([[[3.0, 4.0]], [[1.0, 0.0]]])
+    v = np.array([[[1.0, -1.0]], [[2.0, 3.0]]])
+    g = np.array([[np.log(0.5)], [0.0]])
+    beta = np.array([[0.5], [1.0]])
+    o, H = recurrent_sequence(H0, q, k, v, g, beta, scale=1.0, eps=0.0)
+    np.testing.assert_allclose(o[0, 0], [0.96, 0.6], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[1, 0], np.array([2.96, 3.6]) / np.sqrt(2.0), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(H[0], [[2.0, 3.0], [0.96, 0.6]], rtol=0, atol=1e-14)
+    # chunk form agrees on the same example
+    o2, H2 = chunked_sequence(H0, q, k, v, g, beta, 1.0, 0.0, chunk=2)
+    np.testing.assert_allclose(o2, o, atol=1e-14)
+    np.testing.assert_allclose(H2, H, atol=1e-14)
+
+
+def test_l2_normalize_with_eps_by_hand():
+    # |(3, 4)|^2 = 25; with eps = 11 the denominator is sqrt(36) = 6.
+    np.testing.assert_allclose(l2_normalize(np.array([3.0, 4.0]), 11.0), [0.5, 4.0 / 6.0], atol=1e-15)
+    np.testing.assert_array_equal(l2_normalize(np.zeros(4), 1e-6), np.zeros(4))
+
+
+# ---------------------------------------------------------------------------
+# invariants and closed forms of the rule
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (8, 24), (24, 8)])
+def test_beta0_g0_leaves_state_and_reads_it(dk, dv):
+    rng = np.random.default_rng(10)
+    HK, HV, T = 1, 2, 5
+    H0 = rng.standard_normal((HV, dk, dv))
+    q = rng.standard_normal((T, HK, dk)); k = rng.standard_normal((T, HK, dk))
+    v = rng.standard_normal((T, HV, dv))
+    z = np.zeros((T, HV))
+    scale = dk ** -0.5
+    o, H = recurrent_sequence(H0, q, k, v, z, z, scale, 1e-6)
+    np.testing.assert_array_equal(H, H0)
+    qt = l2_normalize(q, 1e-6)[:, 0] * scale          # [T, dk]
+    np.testing.assert_allclose(o, np.einsum("hij,ti->thj", H0, qt), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (8, 24), (32, 8)])
+def test_unit_key_full_write_reads_back_v(dk, dv):
+    """g = 0, beta = 1, unit k (eps = 0): S k^ = v after the write, and with
+    q = k the output is v * scale (read-out after the write, not before)."""
+    rng = np.random.default_rng(11)
+    H0 = rng.standard_normal((1, dk, dv))
+    k = _unit(rng, 1, 1, dk)
+    v = rng.standard_normal((1, 1, dv))
+    one = np.ones((1, 1))
+    o, H = recurrent_sequence(H0, k, k, v, 0 * one, one, 0.7, 0.0)
+    np.testing.assert_allclose(H[0].T @ k[0, 0], v[0, 0], atol=1e-13)
+    np.testing.assert_allclose(o[0, 0], 0.7 * v[0, 0], atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_delta_write_is_fixed_on_k_and_its_complement(seed):
+    """For unit k the write is fully characterised by its action on k and on
+    the orthogonal complement of k:
+        S1 k = (1 - beta) exp(g) S0 k + beta v,   S1 x = exp(g) S0 x  (x . k = 0).
+    """
+    rng = np.random.default_rng(seed)
+    dk, dv = 12, 7
+    H0 = rng.standard_normal((1, dk, dv))
+    S0 = H0[0].T
+    k = _unit(rng, 1, 1, dk)
+    q = rng.standard_normal((1, 1, dk))
+    v = rng.standard_normal((1, 1, dv))
+    g, beta = -0.37, 0.61
+    o, H = recurrent_sequence(H0, q, k, v, np.array([[g]]), np.array([[beta]]), 1.0, 0.0)
+    S1 = H[0].T
+    kk = k[0, 0]
+    np.testing.assert_allclose(S1 @ kk, (1 - beta) * np.exp(g) * (S0 @ kk) + beta * v[0, 0], atol=1e-13)
+    basis = np.linalg.qr(np.concatenate([kk[:, None], rng.standard_normal((dk, dk - 1))], axis=1))[0][:, 1:]
+    np.testing.assert_allclose(S1 @ basis, np.exp(g) * (S0 @ basis), atol=1e-13)
+    qt = q[0, 0] / np.linalg.norm(q[0, 0])
+    np.testing.assert_allclose(o[0, 0], S1 @ qt, atol=1e-13)
+
+
+def test_pure_decay_closed_form():
+    """beta = 0: H_T = exp(sum g) H0 and o_t = exp(sum_{s<=t} g_s) S0 q~_t."""
+    rng = np.random.default_rng(3)
+    T, HK, HV, dk, dv = 9, 2, 4, 8, 6
+    H0 = rng.standard_normal((HV, dk, dv))
+    q = rng.standard_normal((T, HK, dk)); k = rng.standard_normal((T, HK, dk))
+    v = rng.standard_normal((T, HV, dv))
+    g = -rng.uniform(0.01, 0.5, (T, HV))
+    o, H = recurrent_sequence(H0, q, k, v, g, np.zeros((T, HV)), 0.5, 1e-6)
+    np.testing.assert_allclose(H, np.exp(g.sum(0))[:, None, None] * H0, rtol=1e-13)
+    qt = l2_normalize(q, 1e-6) * 0.5
+    cum = np.exp(np.cumsum(g, 0))
+    for t in range(T):
+        for h in range(HV):
+            np.testing.assert_allclose(o[t, h], cum[t, h] * (H0[h].T @ qt[t, h // 2]), rtol=1e-12, atol=1e-14)
+
+
+def test_associative_memory_with_basis_keys():
+    """g = 0, beta = 1, zero state, keys e_1..e_dk: S = sum_t v_t e_t^T; a
+    later read with q = e_s (beta = 0) returns v_s * scale. dk != dv."""
+    rng = np.random.default_rng(4)
+    dk, dv = 8, 5
+    V = rng.standard_normal((dk, dv))
+    eye = np.eye(dk)
+    T = 2 * dk
+    q = np.concatenate([eye, eye])[:, None, :]
+    k = np.concatenate([eye, eye])[:, None, :]
+    v = np.concatenate([V, rng.standard_normal((dk, dv))])[:, None, :]
+    beta = np.concatenate([np.ones(dk), np.zeros(dk)])[:, None]
+    o, H = recurrent_sequence(np.zeros((1, dk, dv)), q, k, v, np.zeros((T, 1)), beta, 0.25, 0.0)
+    np.testing.assert_allclose(H[0], V, atol=1e-14)              # H = S^T: row i = v_i
+    np.testing.assert_allclose(o[dk:, 0], 0.25 * V, atol=1e-14)
+
+
+def test_full_write_is_idempotent():
+    rng = np.random.default_rng(5)
+    dk, dv = 10, 6
+    H0 = rng.standard_normal((1, dk, dv))
+    k = np.repeat(_unit(rng, 1, 1, dk), 2, axis=0)
+    v = np.repeat(rng.standard_normal((1, 1, dv)), 2, axis=0)
+    q = rng.standard_normal((2, 1, dk))
+    _, H1 = recurrent_sequence(H0, q[:1], k[:1], v[:1], np.zeros((1, 1)), np.ones((1, 1)), 1.0, 0.0)
+    _, H2 = recurrent_sequence(H0, q, k, v, np.zeros((2, 1)), np.ones((2, 1)), 1.0, 0.0)
+    np.testing.assert_allclose(H2, H1, atol=1e-13)
+
+
+def test_linear_in_initial_state_and_values():
+    rng = np.random.default_rng(6)
+    T, HK, HV, dk, dv = 7, 1, 2, 6, 9
+    H0 = rng.standard_normal((HV, dk, dv))
+    q = rng.standard_normal((T, HK, dk)); k = rng.standard_normal((T, HK, dk))
+    v = rng.standard_normal((T, HV, dv))
+    g = -rng.uniform(0, 1, (T, HV)); b = rng.uniform(0, 1, (T, HV))
+    o, H = recurrent_sequence(H0, q, k, v, g, b, 0.3, 1e-6)
+    o1, H1 = recurrent_sequence(H0, q, k, 0 * v, g, b, 0.3, 1e-6)
+    o2, H2 = recurrent_sequence(0 * H0, q, k, v, g, b, 0.3, 1e-6)
+    np.testing.assert_allclose(o, o1 + o2, atol=1e-12)
+    np.testing.assert_allclose(H, H1 + H2, atol=1e-12)
+    o3, H3 = recurrent_sequence(2.5 * H0, q, k, 2.5 * v, g, b, 0.3, 1e-6)
+    np.testing.assert_allclose(o3, 2.5 * o, atol=1e-12)
+
+
+def test_value_columns_are_independent():
+    rng = np.random.default_rng(7)
+    T, dk, dv = 6, 5, 7
+    H0 = rng.standard_normal((1, dk, dv))
+    q = rng.standard_normal((T, 1, dk)); k = rng.standard_normal((T, 1, dk))
+    v = rng.standard_normal((T, 1, dv))
+    g = -rng.uniform(0, 1, (T, 1)); b = rng.uniform(0, 1, (T, 1))
+    perm = rng.permutation(dv)
+    o, H = recurrent_sequence(H0, q, k, v, g, b, 1.0, 1e-6)
+    op, Hp = recurrent_sequence(H0[:, :, perm], q, k, v[:, :, perm], g, b, 1.0, 1e-6)
+    np.testing.assert_allclose(op, o[:, :, perm], atol=1e-13)
+    np.testing.assert_allclose(Hp, H[:, :, perm], atol=1e-13)
+
+
+def test_value_head_reads_key_head_h_div_group():
+    """HK = 2, HV = 4: value head h behaves exactly like a one-head run on key
+    head h // 2, with distinct key heads so a wrong map shows."""
+    rng = np.random.default_rng(8)
+    T, HK, HV, dk, dv = 5, 2, 4, 6, 3
+    H0 = rng.standard_normal((HV, dk, dv))
+    q = rng.standard_normal((T, HK, dk)); k = rng.standard_normal((T, HK, dk))
+    v = rng.standard_normal((T, HV, dv))
+    g = -rng.uniform(0, 1, (T, HV)); b = rng.uniform(0, 1, (T, HV))
+    o, H = recurrent_sequence(H0, q, k, v, g, b, 1.0, 1e-6)
+    for h in range(HV):
+        j = h // 2
+        oh, Hh = recurrent_sequence(H0[h:h + 1], q[:, j:j + 1], k[:, j:j + 1], v[:, h:h + 1],
+                                    g[:, h:h + 1], b[:, h:h + 1], 1.0, 1e-6)
+        np.testing.assert_array_equal(oh[:, 0], o[:, h])
+        np.testing.assert_array_equal(Hh[0], H[h])
+
+
+def test_query_and_key_scale_invariance_and_output_scale():
+    rng = np.random.default_rng(9)
+    T, dk, dv = 4, 8, 8
+    H0 = rng.standard_normal((1, dk, dv))
+    q = rng.standard_normal((T, 1, dk)); k = rng.standard_normal((T, 1, dk))
+    v = rng.standard_normal((T, 1, dv))
+    g = -rng.uniform(0, 1, (T, 1)); b = rng.uniform(0, 1, (T, 1))
+    o, H = recurrent_sequence(H0, q, k, v, g, b, 1.0, 0.0)
+    o2, H2 = recurrent_sequence(H0, 3.0 * q, 0.5 * k, v, g, b, 1.0, 0.0)
+    np.testing.assert_allclose(o2, o, atol=1e-13)
+    np.testing.assert_allclose(H2, H, atol=1e-13)
+    o3, H3 = recurrent_sequence(H0, q, k, v, g, b, dk ** -0.5, 0.0)
+    np.testing.assert_allclose(o3, o * dk ** -0.5, atol=1e-13)
+    np.testing.assert_array_equal(H3, H)
+
+
+# ---------------------------------------------------------------------------
+# two algorithms, one result: chunk form == token loop
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("C", [1, 4, 16, 64])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130])
+def test_chunk_form_equals_token_loop(C, T):
+    rng = np.random.default_rng(100 + T + C)
+    HK, HV, dk, dv = 1, 2, 8, 12
+    H0 = rng.standard_normal((HV, dk, dv)) * 0.3
+    q = rng.standard_normal((T, HK, dk)); k = rng.standard_normal((T, HK, dk))
+    v = rng.standard_normal((T, HV, dv))
+    g = -rng.uniform(0.001, 0.5, (T, HV))
+    b = rng.uniform(0, 1, (T, HV))
+    # extreme and degenerate rows: a very strong decay, beta exactly 0 and 1
+    g[T // 2, 0] = -20.0
+    b[::3, 1] = 0.0
+    b[1::3, 1] = 1.0
+    o, H = recurrent_sequence(H0, q, k, v, g, b, dk ** -0.5, 1e-6)
+    oc, Hc = chunked_sequence(H0, q, k, v, g, b, dk ** -0.5, 1e-6, C)
+    assert _nrm_err(oc, o) < 1e-12
+    assert _nrm_err(Hc, H) < 1e-12
+
+
+def test_chunk_form_equals_token_loop_low_decay_long():
+    rng = np.random.default_rng(12)
+    T, HK, HV, dk, dv = 300, 1, 1, 16, 16
+    H0 = rng.standard_normal((HV, dk, dv))
+    q = rng.standard_normal((T, HK, dk)); k = rng.standard_normal((T, HK, dk))
+    v = rng.standard_normal((T, HV, dv))
+    g = -rng.uniform(1e-4, 1e-2, (T, HV)); b = rng.uniform(0, 1, (T, HV))
+    o, H = recurrent_sequence(H0, q, k, v, g, b, 0.25, 1e-6)
+    oc, Hc = chunked_sequence(H0, q, k, v, g, b, 0.25, 1e-6, 64)
+    assert _nrm_err(oc, o) < 1e-11
+    assert _nrm_err(Hc, H) < 1e-11
+
+
+# ---------------------------------------------------------------------------
+# slot semantics of prefill / decode
+# ---------------------------------------------------------------------------
+
+def _rand_prefill(rng, lengths, HK=1, HV=2, dk=4, dv=3, num_slots=6):
+    T = int(sum(lengths))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    pool = rng.standard_normal((num_slots, HV, dk, dv)).astype(np.float32)
+    q = rng.standard_normal((T, HK, dk)); k = rng.standard_normal((T, HK, dk))
+    v = rng.standard_normal((T, HV, dv))
+    g = -rng.uniform(0, 1, (T, HV)); b = rng.uniform(0, 1, (T, HV))
+    return pool, cu, q, k, v, g, b
+
+
+def test_prefill_slot_semantics():
+    rng = np.random.default_rng(13)
+    lengths = [3, 0, 4, 2, 5]
+    pool, cu, q, k, v, g, b = _rand_prefill(rng, lengths)
+    src = np.array([1, 2, -1, 1, 4])
+    dst = np.array([3, 0, 5, -1, 4])          # last entry in place
+    before = pool.copy()
+    o, new, fin = prefill(pool, cu, src, dst, q, k, v, g, b, 0.5, 1e-6)
+    np.testing.assert_array_equal(pool, before)                # input pool untouched
+    np.testing.assert_array_equal(new[1], before[1])           # shared source untouched
+    np.testing.assert_array_equal(new[2], before[2])           # source of the empty sequence
+    np.testing.assert_array_equal(new[0], before[2])           # length 0: dst <- src
+    assert np.all(np.isnan(o[cu[3]:cu[4]]))                    # dst < 0: skipped
+    np.testing.assert_array_equal(new[np.r_[1, 2]], before[np.r_[1, 2]])
+    # zero initial state for src < 0
+    o2, H2 = recurrent_sequence(np.zeros((2, 4, 3)), q[cu[2]:cu[3]], k[cu[2]:cu[3]], v[cu[2]:cu[3]],
+                                g[cu[2]:cu[3]], b[cu[2]:cu[3]], 0.5, 1e-6)
+    np.testing.assert_array_equal(o[cu[2]:cu[3]], o2)
+    np.testing.assert_array_equal(new[5], H2.astype(np.float32))
+    # in place reads the original bytes
+    o4, H4 = recurrent_sequence(before[4].astype(np.float64), q[cu[4]:], k[cu[4]:], v[cu[4]:],
+                                g[cu[4]:], b[cu[4]:], 0.5, 1e-6)
+    np.testing.assert_array_equal(new[4], H4.astype(np.float32))
+
+
+def test_decode_steps_in_place_equal_one_sequence():
+    """8 decode steps (step 1: src -> dst, then in place on dst) give the
+    outputs and final state of one 8-token prefill from src, up to the fp32
+    rounding of the stored state between steps."""
+    rng = np.random.default_rng(14)
+    pool, cu, q, k, v, g, b = _rand_prefill(rng, [8], HK=1, HV=2, dk=5, dv=7, num_slots=4)
+    o_seq, new_seq, fin = prefill(pool, cu, [1], [2], q, k, v, g, b, 0.4, 1e-6)
+    p = pool
+    outs = []
+    for t in range(8):
+        s = 1 if t == 0 else 2
+        o, p, f = decode_step(p, [s], [2], q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1], b[t:t + 1], 0.4, 1e-6)
+        outs.append(o[0])
+    assert _nrm_err(np.array(outs), o_seq) < 1e-6
+    assert _nrm_err(f[0], fin[0]) < 1e-6
+    np.testing.assert_array_equal(p[1], pool[1])
+    np.testing.assert_array_equal(p[np.r_[0, 3]], pool[np.r_[0, 3]])
+
+
+def test_decode_step_matches_prefill_rows():
+    rng = np.random.default_rng(15)
+    B = 5
+    pool, cu, q, k, v, g, b = _rand_prefill(rng, [1] * B, num_slots=12)
+    src = np.array([0, 1, 1, -1, 4]); dst = np.array([5, 6, 7, 8, 4])
+    o1, p1, _ = decode_step(pool, src, dst, q, k, v, g, b, 0.3, 1e-6)
+    o2, p2, _ = prefill(pool, np.arange(B + 1), src, dst, q, k, v, g, b, 0.3, 1e-6, chunk=64)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(p1, p2, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# slot bookkeeping model
+# ---------------------------------------------------------------------------
+
+def test_slot_model_alloc_lowest_first_all_or_nothing():
+    m = SlotPoolModel(5)
+    assert m.alloc(2) == (GDN_OK, [0, 1])
+    assert m.release(0) == GDN_OK
+    assert m.alloc(2) == (GDN_OK, [0, 2])
+    assert m.alloc(3) == (GDN_E_NO_SLOTS, [])
+    assert m.num_free() == 2                      # failed alloc changed nothing
+    assert m.alloc(-1) == (GDN_E_INVALID, [])
+    assert m.alloc(0) == (GDN_OK, [])
+
+
+def test_slot_model_refcounts_and_cow():
+    m = SlotPoolModel(4)
+    assert m.alloc(1) == (GDN_OK, [0])
+    assert m.cow(0) == (GDN_OK, 0)                # sole holder: in place
+    assert m.retain(0) == GDN_OK
+    assert m.refcount(0) == (GDN_OK, 2)
+    assert m.cow(0) == (GDN_OK, 1)                # shared: fresh slot, source untouched
+    assert m.refcount(0) == (GDN_OK, 2)
+    assert m.cow(-1) == (GDN_OK, 2)               # no source: fresh slot
+    assert m.cow(3) == (GDN_E_SLOT_STATE, -1)     # free slot
+    assert m.cow(4) == (GDN_E_INVALID, -1)
+    assert m.release(3) == GDN_E_SLOT_STATE
+    assert m.retain(3) == GDN_E_SLOT_STATE
+    assert m.retain(-2) == GDN_E_INVALID
+    assert m.release(0) == GDN_OK and m.release(0) == GDN_OK
+    assert m.release(0) == GDN_E_SLOT_STATE       # double release
+    assert m.cow(-1) == (GDN_OK, 0)
+    assert m.cow(-1) == (GDN_OK, 3)
+    assert m.cow(-1) == (GDN_E_NO_SLOTS, -1)
+
+
+def test_slot_model_validate():
+    m = SlotPoolModel(6)
+    m.alloc(5)
+    assert m.validate([0, 0, -1], [1, 2, 3]) == GDN_OK        # shared source
+    assert m.validate([0], [0]) == GDN_OK                      # in place
+    assert m.validate([0, 1], [2, 2]) == GDN_E_ALIAS           # duplicate dst
+    assert m.validate([0, 2], [2, 3]) == GDN_E_ALIAS           # dst is another entry's src
+    assert m.validate([0], [6]) == GDN_E_INVALID               # out of range
+    assert m.validate([5], [1]) == GDN_E_SLOT_STATE            # unallocated source
+    assert m.validate([0], [5]) == GDN_E_SLOT_STATE            # unallocated destination
+    assert m.validate([0, 1], [-1, -1]) == GDN_OK              # padding rows
+    assert m.validate([0], [1, 2]) == GDN_E_INVALID
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 handling of inputs
+# ---------------------------------------------------------------------------
+
+def test_bf16_upcast_is_exact():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x7F7F], np.uint16)
+    vals = bf16_bits_to_f64(bits)
+    np.testing.assert_array_equal(vals[:5], [1.0, -2.0, 1.0078125, 0.0, -0.0])
+    assert vals[5] == (2 - 2 ** -7) * 2.0 ** 127
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20, -1.5], np.float32)
+    np.testing.assert_array_equal(f32_to_bf16_bits(x), np.array([0x3F80, 0x3F82, 0x3F81, 0xBFC0], np.uint16))
