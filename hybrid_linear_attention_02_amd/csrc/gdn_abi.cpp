@@ -1,0 +1,144 @@
+// Argument checking and dispatch of the launching entry points.
+//
+// Everything here runs on the host before any work is enqueued: a call that
+// fails a check returns a GDN_E_* code with a message and enqueues nothing.
+// Slot tables live in device memory and are not read here (that would need a
+// device-to-host round trip); gdn_state_pool_validate checks a host copy, and
+// the kernels skip and flag out-of-range indices.
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "gdn_internal.h"
+
+using gdn::fail;
+
+static bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+static int check_heads(const gdn_pool* pool, int32_t hk, int32_t hv, int32_t dk, int32_t dv, const char* fn) {
+    if (hk <= 0 || hv <= 0 || hv % hk != 0)
+        return fail(GDN_E_INVALID, std::string(fn) + ": num_v_heads must be a positive multiple of num_k_heads");
+    if (hv != pool->num_v_heads || dk != pool->dk || dv != pool->dv)
+        return fail(GDN_E_INVALID, std::string(fn) + ": head shape does not match the pool (HV " +
+                                       std::to_string(pool->num_v_heads) + ", dk " + std::to_string(pool->dk) +
+                                       ", dv " + std::to_string(pool->dv) + ")");
+    return GDN_OK;
+}
+
+extern "C" int gdn_decode_step(const gdn_pool* pool, const gdn_decode_args* a, void* stream) {
+    const char* fn = "gdn_decode_step";
+    if (pool == nullptr || a == nullptr) return fail(GDN_E_INVALID, "gdn_decode_step: NULL pool or args");
+    if (a->batch < 0) return fail(GDN_E_INVALID, "gdn_decode_step: batch must be >= 0");
+    int st = check_heads(pool, a->num_k_heads, a->num_v_heads, a->dk, a->dv, fn);
+    if (st != GDN_OK) return st;
+    if (a->dtype != GDN_DTYPE_F32 && a->dtype != GDN_DTYPE_BF16)
+        return fail(GDN_E_UNSUPPORTED, "gdn_decode_step: dtype must be GDN_DTYPE_F32 or GDN_DTYPE_BF16");
+    if (!std::isfinite(a->scale) || !(a->l2_eps >= 0.0f) || !std::isfinite(a->l2_eps))
+        return fail(GDN_E_INVALID, "gdn_decode_step: scale must be finite and l2_eps finite and >= 0");
+    if (static_cast<int64_t>(a->batch) * a->num_v_heads > INT32_MAX)
+        return fail(GDN_E_INVALID, "gdn_decode_step: batch * num_v_heads too large");
+    if (a->batch == 0) return GDN_OK;
+    const void* ptrs[] = {a->q, a->k, a->v, a->g, a->beta, a->o, a->src_slots, a->dst_slots};
+    for (const void* p : ptrs)
+        if (p == nullptr) return fail(GDN_E_INVALID, "gdn_decode_step: NULL device pointer");
+    const void* vec[] = {a->q, a->k, a->v, a->o};
+    for (const void* p : vec)
+        if (!aligned(p, 16)) return fail(GDN_E_INVALID, "gdn_decode_step: q, k, v, o must be 16-byte aligned");
+    const void* word[] = {a->g, a->beta, a->src_slots, a->dst_slots, a->err_flag};
+    for (const void* p : word)
+        if (!aligned(p, 4)) return fail(GDN_E_INVALID, "gdn_decode_step: g, beta, slot tables, err_flag must be 4-byte aligned");
+    return gdn::launch_decode(pool, a, stream);
+}
+
+extern "C" int gdn_prefill_workspace_bytes(const gdn_pool* pool, const gdn_prefill_args* a, size_t* bytes) {
+    if (bytes == nullptr) return fail(GDN_E_INVALID, "gdn_prefill_workspace_bytes: bytes is NULL");
+    gdn::PrefillPlan plan;
+    const int st = gdn::plan_prefill(pool, a, &plan);
+    if (st != GDN_OK) return st;
+    *bytes = plan.bytes;
+    return GDN_OK;
+}
+
+namespace gdn {
+
+static bool prefill_dims_supported(int32_t dk, int32_t dv) {
+    return (dk == 32 || dk == 64 || dk == 128) && (dv == 16 || dv == 32 || dv == 64 || dv == 128);
+}
+
+int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* plan) {
+    const char* fn = "gdn_prefill_chunked";
+    if (pool == nullptr || a == nullptr) return fail(GDN_E_INVALID, "gdn_prefill_chunked: NULL pool or args");
+    if (a->num_seqs < 0 || a->total_tokens < 0)
+        return fail(GDN_E_INVALID, "gdn_prefill_chunked: num_seqs and total_tokens must be >= 0");
+    int st = check_heads(pool, a->num_k_heads, a->num_v_heads, a->dk, a->dv, fn);
+    if (st != GDN_OK) return st;
+    if (a->chunk_size != 64) return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: chunk_size must be 64");
+    if (a->dtype != GDN_DTYPE_BF16)
+        return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: only GDN_DTYPE_BF16 inputs are built");
+    if (!prefill_dims_supported(a->dk, a->dv))
+        return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: dk must be 32, 64 or 128 and dv 16, 32, 64 or 128");
+    if (!std::isfinite(a->scale) || !(a->l2_eps >= 0.0f) || !std::isfinite(a->l2_eps))
+        return fail(GDN_E_INVALID, "gdn_prefill_chunked: scale must be finite and l2_eps finite and >= 0");
+    const int32_t n = a->num_seqs;
+    int64_t chunks = 0;
+    if (n > 0) {
+        if (a->cu_seqlens_host == nullptr || a->cu_seqlens == nullptr)
+            return fail(GDN_E_INVALID, "gdn_prefill_chunked: cu_seqlens (device and host mirror) required");
+        if (a->cu_seqlens_host[0] != 0) return fail(GDN_E_INVALID, "gdn_prefill_chunked: cu_seqlens[0] must be 0");
+        for (int32_t i = 0; i < n; ++i) {
+            const int64_t len = static_cast<int64_t>(a->cu_seqlens_host[i + 1]) - a->cu_seqlens_host[i];
+            if (len < 0) return fail(GDN_E_INVALID, "gdn_prefill_chunked: cu_seqlens must be non-decreasing");
+            chunks += (len + 63) / 64;
+        }
+        if (a->cu_seqlens_host[n] != a->total_tokens)
+            return fail(GDN_E_INVALID, "gdn_prefill_chunked: cu_seqlens[N] != total_tokens");
+    } else if (a->total_tokens != 0) {
+        return fail(GDN_E_INVALID, "gdn_prefill_chunked: total_tokens must be 0 when num_seqs is 0");
+    }
+    if (chunks * a->num_v_heads > INT32_MAX / 2)
+        return fail(GDN_E_INVALID, "gdn_prefill_chunked: too many chunks");
+    plan->num_chunks = static_cast<int32_t>(chunks);
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    size_t off = 0;
+    plan->off_chunk_offsets = off;
+    off = up(off + sizeof(int32_t) * static_cast<size_t>(n + 1));
+    plan->off_kt = off;
+    off = up(off + 2ull * chunks * a->num_k_heads * a->dk * 64);
+    plan->off_tp = off;
+    off = up(off + 2ull * chunks * a->num_v_heads * 2 * 64 * 64);
+    plan->off_sc = off;
+    off = up(off + 4ull * chunks * a->num_v_heads * (5 * 64));
+    plan->bytes = off;
+    return GDN_OK;
+}
+
+}  // namespace gdn
+
+extern "C" int gdn_prefill_chunked(const gdn_pool* pool, const gdn_prefill_args* a, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    gdn::PrefillPlan plan;
+    int st = gdn::plan_prefill(pool, a, &plan);
+    if (st != GDN_OK) return st;
+    if (a->num_seqs == 0) return GDN_OK;
+    const void* ptrs[] = {a->src_slots, a->dst_slots};
+    for (const void* p : ptrs)
+        if (p == nullptr) return fail(GDN_E_INVALID, "gdn_prefill_chunked: NULL slot table");
+    if (a->total_tokens > 0) {
+        const void* tp[] = {a->q, a->k, a->v, a->g, a->beta, a->o};
+        for (const void* p : tp)
+            if (p == nullptr) return fail(GDN_E_INVALID, "gdn_prefill_chunked: NULL device pointer");
+    }
+    const void* vec[] = {a->q, a->k, a->v, a->o};
+    for (const void* p : vec)
+        if (!aligned(p, 16)) return fail(GDN_E_INVALID, "gdn_prefill_chunked: q, k, v, o must be 16-byte aligned");
+    const void* word[] = {a->g, a->beta, a->src_slots, a->dst_slots, a->err_flag, a->cu_seqlens};
+    for (const void* p : word)
+        if (!aligned(p, 4)) return fail(GDN_E_INVALID, "gdn_prefill_chunked: g, beta, tables, err_flag must be 4-byte aligned");
+    if (workspace == nullptr || !aligned(workspace, 256))
+        return fail(GDN_E_INVALID, "gdn_prefill_chunked: workspace must be non-NULL and 256-byte aligned");
+    if (workspace_bytes < plan.bytes)
+        return fail(GDN_E_INVALID, "gdn_prefill_chunked: workspace too small (need " + std::to_string(plan.bytes) +
+                                       " bytes)");
+    return gdn::launch_prefill(pool, a, plan, workspace, stream);
+}

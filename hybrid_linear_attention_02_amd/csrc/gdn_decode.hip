@@ -1,0 +1,297 @@
+// Single-token decode of the gated delta rule over a slot pool (gfx950).
+//
+// Per (request b, value head h) the update reads the source tile H = S^T
+// (dk x dv float32) once and writes the destination tile once:
+//
+//   a = H^T k^,  c = H^T q~                       (reductions over dk)
+//   u = beta (v - exp(g) a)                       (delta-rule correction)
+//   o = exp(g) c + u (k^ . q~)                    (read-out on the new state)
+//   H' = exp(g) H + k^ u^T                        (decay + rank-one write)
+//
+// which is the rule S <- exp(g) S; S <- S + beta (v - S k^) k^T; o = S q~ with
+// the read-out expanded so that the tile is streamed in a single pass.
+// Source/destination slots come from index tables, so a cached checkpoint is
+// read and never written, and advancing a request moves no state bytes -- the
+// index indirection of the TokenSpeed article (24-ai.news, English), section
+// "What are the key optimizations behind the record?", item "Mamba State
+// Update optimization".
+//
+// The work is bound by HBM bandwidth (about 0.9 flop per byte), so the kernel
+// uses no matrix cores: each thread owns float4 column groups of several rows,
+// loads them with 128-bit non-temporal loads (the tile is touched once), keeps
+// them in registers across the reduction, reduces over dk with cross-lane
+// shuffles and one small LDS exchange between waves, and writes the new tile
+// with 128-bit non-temporal stores.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "gdn_internal.h"
+
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    void* o;
+    float* pool;
+    const int32_t* src;
+    const int32_t* dst;
+    int32_t* err;
+    int32_t hk;
+    int32_t hv;
+    int32_t group;      // hv / hk
+    int32_t num_slots;
+    float scale;
+    float eps;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// float32 -> bfloat16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Element access for the two input types; bf16 is carried as uint16 bits.
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+    static __device__ __forceinline__ float load(const void* p, size_t i) { return static_cast<const float*>(p)[i]; }
+    static __device__ __forceinline__ f4 load4(const void* p, size_t i) {
+        return *reinterpret_cast<const f4*>(static_cast<const float*>(p) + i);
+    }
+    static __device__ __forceinline__ void store4(void* p, size_t i, f4 x) {
+        *reinterpret_cast<f4*>(static_cast<float*>(p) + i) = x;
+    }
+};
+
+template <>
+struct Elem<uint16_t> {
+    static __device__ __forceinline__ float load(const void* p, size_t i) {
+        return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+    }
+    static __device__ __forceinline__ f4 load4(const void* p, size_t i) {
+        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        f4 r;
+        r.x = __uint_as_float(w.x << 16);
+        r.y = __uint_as_float(w.x & 0xffff0000u);
+        r.z = __uint_as_float(w.y << 16);
+        r.w = __uint_as_float(w.y & 0xffff0000u);
+        return r;
+    }
+    static __device__ __forceinline__ void store4(void* p, size_t i, f4 x) {
+        uint2 w;
+        w.x = static_cast<uint32_t>(f32_to_bf16(x.x)) | (static_cast<uint32_t>(f32_to_bf16(x.y)) << 16);
+        w.y = static_cast<uint32_t>(f32_to_bf16(x.z)) | (static_cast<uint32_t>(f32_to_bf16(x.w)) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = w;
+    }
+};
+
+// Thread layout of one (request, head) tile: CG float4 column groups per row,
+// RG row groups; thread t owns column group t % CG of rows t / CG + RG * m.
+constexpr int decode_threads(int dk, int dv) { return (dk * dv / 4 < 256) ? dk * dv / 4 : 256; }
+
+template <int DK, int DV>
+struct DecodeShape {
+    static constexpr int NT = decode_threads(DK, DV);  // threads, a multiple of 64
+    static constexpr int CG = DV / 4;
+    static constexpr int RG = NT / CG;
+    static constexpr int RPT = DK / RG;   // rows per thread
+    static constexpr int NW = NT / 64;    // waves
+    static_assert(NT % 64 == 0 && 64 % CG == 0 && DK % RG == 0, "unsupported tile shape");
+};
+
+template <int DK, int DV, typename T>
+__global__ void __launch_bounds__(decode_threads(DK, DV)) gdn_decode_kernel(DecodeParams p) {
+    using Sh = DecodeShape<DK, DV>;
+    constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NW = Sh::NW;
+    constexpr int KPL = (DK + 63) / 64;   // q/k elements per lane
+
+    __shared__ float s_k[DK];
+    __shared__ float s_q[DK];
+    __shared__ f4 s_red[NW][CG][2];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cg = tid % CG;
+    const int rg = tid / CG;
+    const int b = blockIdx.x / p.hv;
+    const int h = blockIdx.x - b * p.hv;
+
+    const int d = p.dst[b];
+    if (d < 0) return;                       // padding row
+    const int s = p.src[b];
+    if (d >= p.num_slots || s >= p.num_slots) {
+        if (tid == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
+        return;
+    }
+
+    // 1. Issue the whole source tile first; the rest overlaps its latency.
+    f4 st[RPT];
+    if (s >= 0) {
+        const f4* in = reinterpret_cast<const f4*>(p.pool + (static_cast<size_t>(s) * p.hv + h) * (DK * DV));
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) st[m] = __builtin_nontemporal_load(in + (rg + RG * m) * CG + cg);
+    } else {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) st[m] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // 2. L2-normalise k and q of key head h / group (every wave computes the
+    //    sums redundantly; wave 0 publishes the normalised vectors).
+    const int j = h / p.group;
+    const size_t qk_off = (static_cast<size_t>(b) * p.hk + j) * DK;
+    float kx[KPL], qx[KPL];
+    float sk = 0.f, sq = 0.f, skq = 0.f;
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+        const int i = lane + 64 * e;
+        kx[e] = (i < DK) ? Elem<T>::load(p.k, qk_off + i) : 0.f;
+        qx[e] = (i < DK) ? Elem<T>::load(p.q, qk_off + i) : 0.f;
+        sk += kx[e] * kx[e];
+        sq += qx[e] * qx[e];
+        skq += kx[e] * qx[e];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        sk += __shfl_xor(sk, off);
+        sq += __shfl_xor(sq, off);
+        skq += __shfl_xor(skq, off);
+    }
+    const float rk = 1.0f / sqrtf(sk + p.eps);
+    const float rq = p.scale / sqrtf(sq + p.eps);
+    const float kq = skq * rk * rq;          // k^ . q~
+    if (wave == 0) {
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+            const int i = lane + 64 * e;
+            if (i < DK) {
+                s_k[i] = kx[e] * rk;
+                s_q[i] = qx[e] * rq;
+            }
+        }
+    }
+    const size_t gh = static_cast<size_t>(b) * p.hv + h;
+    const float eg = expf(p.g[gh]);
+    const float bt = p.beta[gh];
+    const f4 vv = Elem<T>::load4(p.v, gh * DV + 4 * cg);
+    __syncthreads();
+
+    // 3. Partial H^T k^ and H^T q~ over this thread's rows.
+    f4 a = f4{0.f, 0.f, 0.f, 0.f};
+    f4 c = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int row = rg + RG * m;
+        a += st[m] * s_k[row];
+        c += st[m] * s_q[row];
+    }
+    // 4. Reduce over the row groups: lanes CG apart inside a wave, then the
+    //    waves through LDS, always in the same order (deterministic).
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1) {
+        a.x += __shfl_xor(a.x, off);
+        a.y += __shfl_xor(a.y, off);
+        a.z += __shfl_xor(a.z, off);
+        a.w += __shfl_xor(a.w, off);
+        c.x += __shfl_xor(c.x, off);
+        c.y += __shfl_xor(c.y, off);
+        c.z += __shfl_xor(c.z, off);
+        c.w += __shfl_xor(c.w, off);
+    }
+    if (lane < CG) {
+        s_red[wave][lane][0] = a;
+        s_red[wave][lane][1] = c;
+    }
+    __syncthreads();
+    f4 A = s_red[0][cg][0];
+    f4 C = s_red[0][cg][1];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        A += s_red[w][cg][0];
+        C += s_red[w][cg][1];
+    }
+
+    // 5. Delta correction, output, and the new tile.
+    const f4 u = bt * (vv - eg * A);
+    if (rg == 0) Elem<T>::store4(p.o, gh * DV + 4 * cg, eg * C + kq * u);
+    f4* out = reinterpret_cast<f4*>(p.pool + (static_cast<size_t>(d) * p.hv + h) * (DK * DV));
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int row = rg + RG * m;
+        const f4 nv = eg * st[m] + s_k[row] * u;
+        __builtin_nontemporal_store(nv, out + row * CG + cg);
+    }
+}
+
+template <int DK, int DV, typename T>
+int launch_shape(const gdn_pool* pool, const gdn_decode_args* a, hipStream_t stream) {
+    DecodeParams p;
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.g = a->g;
+    p.beta = a->beta;
+    p.o = a->o;
+    p.pool = pool->storage;
+    p.src = a->src_slots;
+    p.dst = a->dst_slots;
+    p.err = a->err_flag;
+    p.hk = a->num_k_heads;
+    p.hv = a->num_v_heads;
+    p.group = a->num_v_heads / a->num_k_heads;
+    p.num_slots = pool->num_slots;
+    p.scale = a->scale;
+    p.eps = a->l2_eps;
+    const dim3 grid(static_cast<unsigned>(a->batch) * static_cast<unsigned>(a->num_v_heads));
+    hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, T>), grid, dim3(DecodeShape<DK, DV>::NT), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return gdn::fail(GDN_E_HIP, std::string("gdn_decode_step: launch failed: ") + hipGetErrorString(e));
+    return GDN_OK;
+}
+
+template <typename T>
+int dispatch_dv(const gdn_pool* pool, const gdn_decode_args* a, hipStream_t s) {
+#define GDN_DK_CASE(DK)                                               \
+    if (a->dk == DK) {                                                \
+        switch (a->dv) {                                              \
+            case 16: return launch_shape<DK, 16, T>(pool, a, s);     \
+            case 32: return launch_shape<DK, 32, T>(pool, a, s);     \
+            case 64: return launch_shape<DK, 64, T>(pool, a, s);     \
+            case 128: return launch_shape<DK, 128, T>(pool, a, s);   \
+            default: break;                                           \
+        }                                                             \
+    }
+    GDN_DK_CASE(16)
+    GDN_DK_CASE(32)
+    GDN_DK_CASE(64)
+    GDN_DK_CASE(128)
+#undef GDN_DK_CASE
+    return gdn::fail(GDN_E_UNSUPPORTED, "gdn_decode_step: unsupported dk/dv");
+}
+
+}  // namespace
+
+namespace gdn {
+
+int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a->dtype == GDN_DTYPE_F32) return dispatch_dv<float>(pool, a, s);
+    return dispatch_dv<uint16_t>(pool, a, s);
+}
+
+}  // namespace gdn

@@ -1,0 +1,43 @@
+// Internal declarations shared by the translation units of libgdn.so.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+#include <set>
+
+#include "gdn.h"
+
+struct gdn_pool {
+    int32_t num_slots = 0;
+    int32_t num_v_heads = 0;
+    int32_t dk = 0;
+    int32_t dv = 0;
+    float* storage = nullptr;          // caller-owned device memory
+    std::vector<int32_t> ref;          // refcount per slot (0 = free)
+    std::set<int32_t> free_slots;      // ordered: lowest index first
+};
+
+namespace gdn {
+
+// Record a failure message for gdn_last_error() and return `code`.
+int fail(int code, const std::string& msg);
+
+// Kernel launchers (defined in the .hip files). They assume validated
+// arguments and return GDN_OK or GDN_E_HIP / GDN_E_UNSUPPORTED.
+int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream);
+
+struct PrefillPlan {
+    int32_t num_chunks = 0;       // sum over sequences of ceil(len / 64)
+    size_t off_chunk_offsets = 0; // int32 [N+1]: first chunk index of each sequence
+    size_t off_kt = 0;            // bf16 [chunks][HK][dk][64]: K^T per chunk
+    size_t off_tp = 0;            // bf16 [chunks][HV][2][64][64]: T and P
+    size_t off_sc = 0;            // float [chunks][HV][4][64] + gamma_last
+    size_t bytes = 0;
+};
+int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* plan);
+int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const PrefillPlan& plan,
+                   void* workspace, void* stream);
+
+}  // namespace gdn

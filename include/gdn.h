@@ -1,0 +1,196 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the recurrent-state update of Gated Delta
+ * Network (GDN) linear-attention layers on AMD MI355X (gfx950).
+ *
+ * The operation. The TokenSpeed article (24-ai.news, English, "PyTorch:
+ * TokenSpeed achieves record 580 tokens/s on Qwen3.5-397B-A17B ...", section
+ * "What is TokenSpeed and how does it differ from vLLM?") names linear-attention
+ * layers built on the Gated Delta Network inside a hybrid model; the pages do
+ * not print the recurrence. This library implements the gated delta rule, per
+ * token and per value head, with S the dv x dk state matrix:
+ *
+ *     k^ = k / sqrt(|k|^2 + l2_eps)        q~ = q / sqrt(|q|^2 + l2_eps) * scale
+ *     S  <- exp(g) S
+ *     S  <- S + beta (v - S k^) k^T
+ *     o   = S q~
+ *
+ * Slots and index indirection. Same article, section "What are the key
+ * optimizations behind the record?", items "Hybrid prefix caching for
+ * GDN/Mamba" (state reuse under copy-on-write) and "Mamba State Update
+ * optimization" (index indirection in place of copying state between steps);
+ * zubnet.ai (Portuguese), "LightSeek TokenSpeed ...", second paragraph (the
+ * linear-attention state is checkpointed beside the KV pages and cached
+ * checkpoints are reused without mutation). Here states live in a pool of
+ * fixed-size slots; every request names a source slot that is only read and a
+ * destination slot that is written, so advancing a request is an index write
+ * and a cached checkpoint is never modified.
+ *
+ * Storage. A pool is caller-owned device memory of
+ *     num_slots * HV * dk * dv  float32,  layout [slot][HV][dk][dv],
+ * each (slot, head) tile holding H = S^T row-major (dk rows of dv floats).
+ * q and k are [tokens][HK][dk]; v and o are [tokens][HV][dv]; g and beta are
+ * float32 [tokens][HV]. Value head h reads key/query head h / (HV / HK).
+ *
+ * Conventions shared by every call:
+ *   - Return value: GDN_OK (0) or a negative GDN_E_* code. A failing call
+ *     changes no state; gdn_last_error() then returns a message (thread-local,
+ *     valid until the next failing call on the same thread).
+ *   - Device pointers are HIP device addresses; "stream" is a hipStream_t
+ *     passed as void* (NULL = the default stream). Launching calls are
+ *     asynchronous: they enqueue work on the stream, never synchronise the
+ *     host, never allocate, and may be captured into a HIP graph.
+ *   - Pool bookkeeping calls are host-only and touch no device memory. They
+ *     are not thread-safe; one scheduler thread serialises them.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define GDN_OK             0
+#define GDN_E_INVALID     -1  /* null pointer, bad size, bad alignment, index out of range */
+#define GDN_E_UNSUPPORTED -2  /* a dtype / head-size combination this build has no kernel for */
+#define GDN_E_NO_SLOTS    -3  /* not enough free slots; nothing was allocated */
+#define GDN_E_SLOT_STATE  -4  /* slot is free where an allocated slot is required */
+#define GDN_E_ALIAS       -5  /* a destination is repeated or is another entry's source */
+#define GDN_E_HIP         -6  /* the HIP runtime reported an error (message copied) */
+
+/* element types of q, k, v and o (g, beta and the pool are always float32) */
+#define GDN_DTYPE_F32  0
+#define GDN_DTYPE_BF16 1
+
+/* bits of the optional device error flag (int32, set by kernels, never cleared) */
+#define GDN_ERRFLAG_SLOT_RANGE 1   /* a src/dst slot index >= num_slots was skipped */
+
+typedef struct gdn_pool gdn_pool;   /* opaque host-side handle */
+
+/* ------------------------------------------------------------------------ */
+/* slot pool (host bookkeeping over caller-owned device storage)             */
+/* ------------------------------------------------------------------------ */
+
+/* Create a pool handle over `storage` (device, caller-owned, >= 16-byte
+ * aligned, num_slots*num_v_heads*dk*dv floats). The pool never frees or reads
+ * the storage itself; all slots start free (refcount 0).
+ * dk, dv must be in {16, 32, 64, 128}. Errors: GDN_E_INVALID. */
+int gdn_state_pool_create(int32_t num_slots, int32_t num_v_heads, int32_t dk, int32_t dv,
+                          float* storage, gdn_pool** out);
+
+/* Free the host bookkeeping (not the storage). NULL is accepted. */
+int gdn_state_pool_destroy(gdn_pool* pool);
+
+/* Allocate n slots, lowest free indices first, each with refcount 1, written
+ * to out[0..n-1] (host). All or nothing: GDN_E_NO_SLOTS leaves the pool
+ * unchanged. n < 0 or out == NULL with n > 0: GDN_E_INVALID. */
+int gdn_state_pool_alloc(gdn_pool* pool, int32_t n, int32_t* out);
+
+/* refcount += 1 / -= 1 (the slot becomes free at 0). Out of range:
+ * GDN_E_INVALID; slot free: GDN_E_SLOT_STATE. */
+int gdn_state_pool_retain(gdn_pool* pool, int32_t slot);
+int gdn_state_pool_release(gdn_pool* pool, int32_t slot);
+
+/* Copy-on-write target for a caller about to advance state read from `src`:
+ * if src >= 0 and refcount(src) == 1 the caller is its only holder and *dst =
+ * src (update in place); if src < 0 (no state) or refcount(src) > 1 a fresh
+ * slot is allocated (refcount 1). The refcount of src is never changed and no
+ * state bytes move: the O(1) pointer update of the pages. Errors:
+ * GDN_E_INVALID (src >= num_slots, dst NULL), GDN_E_SLOT_STATE (src free),
+ * GDN_E_NO_SLOTS. */
+int gdn_state_pool_cow(gdn_pool* pool, int32_t src, int32_t* dst);
+
+/* Check a slot table (host copies of what the kernels will read).
+ * Pass 1, entry by entry (src before dst): index >= num_slots ->
+ * GDN_E_INVALID; non-negative index of a free slot -> GDN_E_SLOT_STATE.
+ * Pass 2: a destination used twice, or equal to a different entry's source ->
+ * GDN_E_ALIAS. A source shared by several entries, src == dst in one entry
+ * (in place) and negative indices (none) are allowed. Kernels assume a table
+ * that passed this check and do not re-check aliasing. */
+int gdn_state_pool_validate(const gdn_pool* pool, int32_t n, const int32_t* src_host,
+                            const int32_t* dst_host);
+
+/* queries */
+int gdn_state_pool_refcount(const gdn_pool* pool, int32_t slot, int32_t* out);
+int gdn_state_pool_num_free(const gdn_pool* pool, int32_t* out);
+int gdn_state_pool_capacity(const gdn_pool* pool, int32_t* out);
+
+/* ------------------------------------------------------------------------ */
+/* decode: one token per request                                             */
+/* ------------------------------------------------------------------------ */
+
+typedef struct gdn_decode_args {
+    int32_t batch;          /* B >= 0 requests */
+    int32_t num_k_heads;    /* HK, divides num_v_heads */
+    int32_t num_v_heads;    /* HV, must equal the pool's */
+    int32_t dk, dv;         /* must equal the pool's */
+    int32_t dtype;          /* GDN_DTYPE_F32 or GDN_DTYPE_BF16: q, k, v, o */
+    const void* q;          /* [B][HK][dk] device */
+    const void* k;          /* [B][HK][dk] device */
+    const void* v;          /* [B][HV][dv] device */
+    const float* g;         /* [B][HV] device, log-decay (<= 0 expected) */
+    const float* beta;      /* [B][HV] device */
+    void* o;                /* [B][HV][dv] device, written for rows with dst >= 0 */
+    const int32_t* src_slots;  /* [B] device: < 0 = zero initial state */
+    const int32_t* dst_slots;  /* [B] device: < 0 = padding row, skipped */
+    float scale;            /* applied to q after normalisation (usually dk^-1/2) */
+    float l2_eps;           /* epsilon of the q/k L2 normalisation */
+    int32_t* err_flag;      /* optional device int32; GDN_ERRFLAG_* bits OR-ed in */
+} gdn_decode_args;
+
+/* Advance every request by one token: o[b] = read-out after the update;
+ * pool[dst[b]] = updated state; pool[src[b]] untouched unless src == dst.
+ * All device pointers >= 16-byte aligned. Slot indices >= num_slots are
+ * skipped in the kernel and flagged in err_flag. Asynchronous on `stream`,
+ * no allocation, no host synchronisation, graph-capturable. */
+int gdn_decode_step(const gdn_pool* pool, const gdn_decode_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* chunked prefill: variable-length sequences packed by cu_seqlens           */
+/* ------------------------------------------------------------------------ */
+
+typedef struct gdn_prefill_args {
+    int32_t num_seqs;             /* N >= 0 */
+    int32_t total_tokens;         /* T = cu_seqlens[N] */
+    const int32_t* cu_seqlens;    /* [N+1] device, 0 = cu[0] <= cu[1] <= ... */
+    const int32_t* cu_seqlens_host; /* [N+1] host mirror (grid sizing, checks) */
+    int32_t chunk_size;           /* must be 64 */
+    int32_t num_k_heads, num_v_heads, dk, dv;
+    int32_t dtype;                /* GDN_DTYPE_BF16 (fp32 prefill: GDN_E_UNSUPPORTED) */
+    const void* q;                /* [T][HK][dk] device */
+    const void* k;                /* [T][HK][dk] device */
+    const void* v;                /* [T][HV][dv] device */
+    const float* g;               /* [T][HV] device */
+    const float* beta;            /* [T][HV] device */
+    void* o;                      /* [T][HV][dv] device */
+    const int32_t* src_slots;     /* [N] device: < 0 = zero initial state */
+    const int32_t* dst_slots;     /* [N] device: < 0 = sequence skipped */
+    float scale;
+    float l2_eps;
+    int32_t* err_flag;            /* optional, as for decode */
+} gdn_prefill_args;
+
+/* Bytes of device workspace gdn_prefill_chunked needs for these args (depends
+ * on N, the chunk count from cu_seqlens_host, and the head shape). */
+int gdn_prefill_workspace_bytes(const gdn_pool* pool, const gdn_prefill_args* args, size_t* bytes);
+
+/* Run every sequence through the rule from its source state and write the
+ * final state to its destination slot. Chunks of 64 tokens restart at every
+ * sequence boundary; a zero-length sequence copies the source state (zero if
+ * src < 0) to the destination. `workspace` is caller-owned device memory of
+ * at least gdn_prefill_workspace_bytes, 256-byte aligned; its contents are
+ * scratch. Asynchronous on `stream`, no allocation, no host sync. */
+int gdn_prefill_chunked(const gdn_pool* pool, const gdn_prefill_args* args, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

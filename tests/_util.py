@@ -1,0 +1,70 @@
+"""Shared helpers of the GPU tests: moving workload arrays to the device and
+applying the parity tolerances. No state-update arithmetic lives here."""
+
+import numpy as np
+
+from oracle import bf16_bits_to_f64
+
+
+def to_dev(x, dtype_name):
+    """numpy workload array -> device tensor (bf16 arrays arrive as uint16 bits)."""
+    import torch
+    if dtype_name == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.cuda()
+
+
+def as_f64(x, dtype_name):
+    """Workload array -> exact float64 values as the GPU sees them."""
+    if dtype_name == "bf16":
+        return bf16_bits_to_f64(x)
+    return np.asarray(x, np.float64)
+
+
+def out_f64(t):
+    """Device output tensor (f32 or bf16) -> float64 numpy."""
+    import torch
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def normwise_err(x, ref):
+    """max|x - ref| / max|ref| (normwise, robust near zero)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(x - ref)) / den) if den > 0 else float(np.max(np.abs(x)))
+
+
+def rel_frob(x, ref):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / den) if den > 0 else float(np.linalg.norm(x))
+
+
+# Tolerances of the parity bar.
+FP32_REL = 1e-5          # fp32 inputs: max|x - y| <= 1e-5 max|y|, per tensor / step / slot
+BF16_OUT_ABS = 2e-2      # bf16 inputs: max|o - o_ref| <= 2e-2
+BF16_STATE_FROB = 1e-2   # bf16 inputs: ||H - H_ref||_F / ||H_ref||_F <= 1e-2 per destination slot
+
+
+def check_outputs(o_gpu, o_ref, dtype_name, what=""):
+    if dtype_name == "f32":
+        e = normwise_err(o_gpu, o_ref)
+        assert e <= FP32_REL, f"{what} fp32 output normwise error {e:.3e}"
+        return e
+    e = float(np.max(np.abs(np.asarray(o_gpu) - np.asarray(o_ref)))) if np.size(o_ref) else 0.0
+    assert e <= BF16_OUT_ABS, f"{what} bf16 output max-abs error {e:.3e}"
+    return e
+
+
+def check_state(h_gpu, h_ref, dtype_name, what=""):
+    if dtype_name == "f32":
+        e = normwise_err(h_gpu, h_ref)
+        assert e <= FP32_REL, f"{what} fp32 state normwise error {e:.3e}"
+        return e
+    e = rel_frob(h_gpu, h_ref)
+    assert e <= BF16_STATE_FROB, f"{what} bf16 state relative Frobenius error {e:.3e}"
+    return e

@@ -1,0 +1,272 @@
+"""Host-side tests of libgdn.so: exports, slot bookkeeping, argument checks.
+
+No GPU is needed: the pool's bookkeeping never touches device memory, and every
+argument check here fails (or returns early) before anything is enqueued. Fake
+"device" addresses are plain aligned host addresses that are never read.
+"""
+
+import ctypes
+import os
+import re
+from ctypes import POINTER, byref, c_int32, c_size_t, c_void_p
+
+import numpy as np
+import pytest
+from hypothesis import settings, strategies as st
+from hypothesis.stateful import RuleBasedStateMachine, invariant, precondition, rule
+
+from oracle import SlotPoolModel
+from hybrid_linear_attention_02_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn.so is not built; run __graft_entry__.build() first")
+    return gdn.load_library()
+
+
+def _fake_storage(nbytes=1 << 12):
+    buf = np.zeros(nbytes // 4 + 64, np.float32)
+    addr = buf.ctypes.data
+    off = (-addr) % 256
+    return buf, addr + off
+
+
+def _make_pool(lib, num_slots=8, hv=2, dk=16, dv=16):
+    buf, addr = _fake_storage()
+    h = c_void_p()
+    assert lib.gdn_state_pool_create(num_slots, hv, dk, dv, c_void_p(addr), byref(h)) == gdn.GDN_OK
+    return buf, h
+
+
+def test_every_declared_symbol_is_exported(lib):
+    header = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    declared = set(re.findall(r"^(?:int|const char\*)\s+(gdn_\w+)\s*\(", header, re.M))
+    assert declared == set(gdn.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_create_rejects_bad_arguments(lib):
+    buf, addr = _fake_storage()
+    h = c_void_p()
+    cases = [(0, 2, 16, 16, addr), (4, 0, 16, 16, addr), (4, 2, 24, 16, addr), (4, 2, 16, 256, addr),
+             (4, 2, 16, 16, None), (4, 2, 16, 16, addr + 4)]
+    for ns, hv, dk, dv, p in cases:
+        assert lib.gdn_state_pool_create(ns, hv, dk, dv, c_void_p(p), byref(h)) == gdn.GDN_E_INVALID
+        assert lib.gdn_last_error() != b""
+    assert lib.gdn_state_pool_create(4, 2, 16, 16, c_void_p(addr), None) == gdn.GDN_E_INVALID
+
+
+def _alloc(lib, h, n):
+    out = (c_int32 * max(n, 1))()
+    st_ = lib.gdn_state_pool_alloc(h, n, out)
+    return st_, ([int(out[i]) for i in range(n)] if st_ == 0 else [])
+
+
+class PoolMachine(RuleBasedStateMachine):
+    """Drive the C++ pool and the Python model with the same operations and
+    require identical status codes, slot ids, refcounts and free counts."""
+
+    CAP = 9
+
+    def __init__(self):
+        super().__init__()
+        self.lib = gdn.load_library()
+        self.buf, self.h = _make_pool(self.lib, num_slots=self.CAP)
+        self.model = SlotPoolModel(self.CAP)
+
+    def teardown(self):
+        self.lib.gdn_state_pool_destroy(self.h)
+
+    slot = st.integers(min_value=-2, max_value=CAP + 1)
+
+    @rule(n=st.integers(min_value=-1, max_value=CAP + 1))
+    def alloc(self, n):
+        got = _alloc(self.lib, self.h, n)
+        assert got == self.model.alloc(n)
+
+    @rule(s=slot)
+    def retain(self, s):
+        assert self.lib.gdn_state_pool_retain(self.h, s) == self.model.retain(s)
+
+    @rule(s=slot)
+    def release(self, s):
+        assert self.lib.gdn_state_pool_release(self.h, s) == self.model.release(s)
+
+    @rule(s=slot)
+    def cow(self, s):
+        d = c_int32(-1)
+        st_ = self.lib.gdn_state_pool_cow(self.h, s, byref(d))
+        mst, md = self.model.cow(s)
+        assert st_ == mst
+        if st_ == 0:
+            assert d.value == md
+
+    @rule(src=st.lists(slot, min_size=0, max_size=5), data=st.data())
+    def validate(self, src, data):
+        dst = data.draw(st.lists(self.slot, min_size=len(src), max_size=len(src)))
+        s = np.asarray(src, np.int32)
+        d = np.asarray(dst, np.int32)
+        got = self.lib.gdn_state_pool_validate(self.h, len(s), s.ctypes.data_as(POINTER(c_int32)),
+                                               d.ctypes.data_as(POINTER(c_int32)))
+        assert got == self.model.validate(src, dst)
+
+    @invariant()
+    def counts_agree(self):
+        r = c_int32()
+        assert self.lib.gdn_state_pool_num_free(self.h, byref(r)) == 0
+        assert r.value == self.model.num_free()
+        assert self.lib.gdn_state_pool_capacity(self.h, byref(r)) == 0 and r.value == self.CAP
+        for s in range(self.CAP):
+            assert self.lib.gdn_state_pool_refcount(self.h, s, byref(r)) == 0
+            assert r.value == self.model.ref[s]
+
+
+PoolMachine.TestCase.settings = settings(max_examples=150, stateful_step_count=40, deadline=None)
+TestPoolMachine = PoolMachine.TestCase
+
+
+def test_pool_refcount_query_errors(lib):
+    buf, h = _make_pool(lib)
+    r = c_int32()
+    assert lib.gdn_state_pool_refcount(h, 8, byref(r)) == gdn.GDN_E_INVALID
+    assert lib.gdn_state_pool_refcount(h, -1, byref(r)) == gdn.GDN_E_INVALID
+    assert lib.gdn_state_pool_num_free(None, byref(r)) == gdn.GDN_E_INVALID
+    assert lib.gdn_state_pool_alloc(h, 1, None) == gdn.GDN_E_INVALID
+    assert lib.gdn_state_pool_destroy(None) == gdn.GDN_OK
+    lib.gdn_state_pool_destroy(h)
+
+
+# ---------------------------------------------------------------------------
+# argument checks of the launching calls (nothing is ever enqueued here)
+# ---------------------------------------------------------------------------
+
+def _decode_args(addr, **kw):
+    a = gdn.DecodeArgs()
+    a.batch, a.num_k_heads, a.num_v_heads, a.dk, a.dv, a.dtype = 4, 1, 2, 16, 16, gdn.GDN_DTYPE_F32
+    for f in ("q", "k", "v", "g", "beta", "o", "src_slots", "dst_slots"):
+        setattr(a, f, addr)
+    a.scale, a.l2_eps, a.err_flag = 0.25, 1e-6, None
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(batch=-1), gdn.GDN_E_INVALID),
+    (dict(num_k_heads=0), gdn.GDN_E_INVALID),
+    (dict(num_k_heads=3, num_v_heads=2), gdn.GDN_E_INVALID),
+    (dict(num_v_heads=4, num_k_heads=1), gdn.GDN_E_INVALID),   # pool has HV = 2
+    (dict(dk=32), gdn.GDN_E_INVALID),                          # pool has dk = 16
+    (dict(dtype=7), gdn.GDN_E_UNSUPPORTED),
+    (dict(q=None), gdn.GDN_E_INVALID),
+    (dict(dst_slots=None), gdn.GDN_E_INVALID),
+    (dict(l2_eps=-1.0), gdn.GDN_E_INVALID),
+    (dict(scale=float("inf")), gdn.GDN_E_INVALID),
+    ("misaligned_v", gdn.GDN_E_INVALID),
+    ("misaligned_g", gdn.GDN_E_INVALID),
+])
+def test_decode_argument_errors(lib, change, code):
+    buf, h = _make_pool(lib)
+    _, addr = _fake_storage()
+    if change == "misaligned_v":
+        a = _decode_args(addr, v=addr + 8)
+    elif change == "misaligned_g":
+        a = _decode_args(addr, g=addr + 2)
+    else:
+        a = _decode_args(addr, **change)
+    assert lib.gdn_decode_step(h, byref(a), None) == code
+    assert len(lib.gdn_last_error()) > 0
+    lib.gdn_state_pool_destroy(h)
+
+
+def test_decode_empty_batch_is_a_no_op(lib):
+    buf, h = _make_pool(lib)
+    a = _decode_args(None, batch=0)
+    assert lib.gdn_decode_step(h, byref(a), None) == gdn.GDN_OK
+    assert lib.gdn_decode_step(None, byref(a), None) == gdn.GDN_E_INVALID
+    lib.gdn_state_pool_destroy(h)
+
+
+def _prefill_args(addr, cu_host, **kw):
+    a = gdn.PrefillArgs()
+    a.num_seqs = len(cu_host) - 1
+    a.total_tokens = int(cu_host[-1])
+    a.cu_seqlens, a.cu_seqlens_host = addr, cu_host.ctypes.data
+    a.chunk_size, a.num_k_heads, a.num_v_heads, a.dk, a.dv, a.dtype = 64, 1, 2, 128, 128, gdn.GDN_DTYPE_BF16
+    for f in ("q", "k", "v", "g", "beta", "o", "src_slots", "dst_slots"):
+        setattr(a, f, addr)
+    a.scale, a.l2_eps, a.err_flag = 0.1, 1e-6, None
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+def test_prefill_workspace_size_grows_with_chunks(lib):
+    buf, h = _make_pool(lib, hv=2, dk=128, dv=128)
+    _, addr = _fake_storage()
+    sizes = []
+    for cu in ([0, 64], [0, 65], [0, 64, 64, 200]):
+        cuh = np.asarray(cu, np.int32)
+        a = _prefill_args(addr, cuh)
+        n = c_size_t()
+        assert lib.gdn_prefill_workspace_bytes(h, byref(a), byref(n)) == gdn.GDN_OK
+        assert n.value % 256 == 0
+        sizes.append(n.value)
+    assert sizes[0] < sizes[1] < sizes[2]
+    lib.gdn_state_pool_destroy(h)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(chunk_size=32), gdn.GDN_E_UNSUPPORTED),
+    (dict(dtype=gdn.GDN_DTYPE_F32), gdn.GDN_E_UNSUPPORTED),
+    (dict(total_tokens=5), gdn.GDN_E_INVALID),
+    (dict(cu_seqlens_host=None), gdn.GDN_E_INVALID),
+    (dict(q=None), gdn.GDN_E_INVALID),
+    (dict(src_slots=None), gdn.GDN_E_INVALID),
+    ("bad_cu", gdn.GDN_E_INVALID),
+    ("small_ws", gdn.GDN_E_INVALID),
+    ("misaligned_ws", gdn.GDN_E_INVALID),
+])
+def test_prefill_argument_errors(lib, change, code):
+    buf, h = _make_pool(lib, hv=2, dk=128, dv=128)
+    _, addr = _fake_storage()
+    cuh = np.asarray([0, 10, 70], np.int32)
+    ws, ws_addr = _fake_storage(1 << 16)
+    ws_bytes = 1 << 15
+    if change == "bad_cu":
+        bad = np.asarray([0, 80, 70], np.int32)
+        a = _prefill_args(addr, bad, total_tokens=70)
+    elif change == "small_ws":
+        a = _prefill_args(addr, cuh)
+        ws_bytes = 256
+    elif change == "misaligned_ws":
+        a = _prefill_args(addr, cuh)
+        ws_addr += 16
+    else:
+        a = _prefill_args(addr, cuh, **change)
+    assert lib.gdn_prefill_chunked(h, byref(a), c_void_p(ws_addr), ws_bytes, None) == code
+    assert len(lib.gdn_last_error()) > 0
+    lib.gdn_state_pool_destroy(h)
+
+
+def test_prefill_no_sequences_is_a_no_op(lib):
+    buf, h = _make_pool(lib, hv=2, dk=128, dv=128)
+    cuh = np.asarray([0], np.int32)
+    a = _prefill_args(None, cuh)
+    assert lib.gdn_prefill_chunked(h, byref(a), None, 0, None) == gdn.GDN_OK
+    lib.gdn_state_pool_destroy(h)
+
+
+def test_prefill_unsupported_head_dim(lib):
+    buf, h = _make_pool(lib, hv=2, dk=16, dv=16)
+    _, addr = _fake_storage()
+    cuh = np.asarray([0, 8], np.int32)
+    a = _prefill_args(addr, cuh, dk=16, dv=16)
+    n = c_size_t()
+    assert lib.gdn_prefill_workspace_bytes(h, byref(a), byref(n)) == gdn.GDN_E_UNSUPPORTED
+    lib.gdn_state_pool_destroy(h)
