@@ -1,0 +1,303 @@
+"""Throughput of the GDN state update on one MI355X, as one JSON line.
+
+Primary line: batched decode -- 64 requests, 16 key / 32 value heads, 128 x 128
+fp32 state tiles in a 256-slot pool, bf16 q/k/v -- one step = one
+gdn_decode_step over the batch (slot resolution, normalisation, decay, delta
+write, read-out, state store). The first timed step reads the source slots and
+writes fresh destination slots; later steps update those in place. `value` is
+algorithmic bytes per second over the K timed steps (inputs resident in HBM).
+
+Also measured in the same run (the metric has two halves):
+  * chunked prefill of one 8192-token bf16 sequence (same head shape), reported
+    under "prefill" as tokens/s and algorithmic MFMA flops against the bf16
+    dense peak;
+  * the fp64 CPU oracle on a bounded sample of the decode workload
+    ("cpu_baseline", rank 0, one GPU only).
+
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "GDN decode state-update HBM GB/s (% peak); chunked prefill tokens/s (MFMA %)"
+
+
+def decode_bytes_per_request(HK, HV, dk, dv, elem):
+    """Algorithmic HBM bytes of one request-step: state tile in and out (fp32),
+    q and k, v and o, g and beta (fp32), the two slot indices."""
+    return 2 * HV * dk * dv * 4 + 2 * HK * dk * elem + 2 * HV * dv * elem + 8 * HV + 8
+
+
+def prefill_flops_per_token(HV, dk, dv, C=64, G=2):
+    """Algorithmic MFMA flops per token of the chunk form (full chunks): W, U',
+    U, inter-chunk output, intra-chunk output, state advance, shared Grams."""
+    return HV * (2 * C * dk + 4 * C * dv + 6 * dk * dv + 4 * C * dk // G)
+
+
+def prefill_bytes_per_token(HK, HV, dk, dv, elem=2):
+    return 2 * HK * dk * elem + 2 * HV * dv * elem + 8 * HV
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "hybrid_linear_attention_02_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(profile_name, src_names, launches_bytes_key):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, or
+    None when the summary is missing or was taken on a different kernel."""
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != _src_hash(*src_names):
+        return None
+    try:
+        return float(vals[launches_bytes_key])
+    except (KeyError, ValueError):
+        return None
+
+
+def bench_decode(steps, warmup):
+    import torch
+    from hybrid_linear_attention_02_amd import gdn
+    from hybrid_linear_attention_02_amd.workloads import batched_decode
+
+    wl = batched_decode(steps=max(steps, 1) + warmup)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    inputs = [(bf(t.q), bf(t.k), bf(t.v), dev(t.g), dev(t.beta)) for t in wl.steps]
+    init = dev(wl.pool)
+    storage = init.clone()
+    pool = gdn.gdn_state_pool_create(wl.num_slots, wl.HV, wl.dk, wl.dv, storage=storage)
+    # sources hold checkpoints; destinations come off the free list
+    pool.alloc(wl.num_slots)
+    keep = set(int(s) for s in wl.src)
+    for s in range(wl.num_slots):
+        if s not in keep:
+            pool.release(s)
+    dst = pool.alloc(wl.B)
+    pool.validate(list(wl.src), dst)
+    src_t = torch.tensor(wl.src, dtype=torch.int32, device="cuda")
+    dst_t = torch.tensor(dst, dtype=torch.int32, device="cuda")
+    o = torch.empty((wl.B, wl.HV, wl.dv), dtype=torch.bfloat16, device="cuda")
+
+    def step(i, first):
+        q, k, v, g, b = inputs[i]
+        gdn.gdn_decode_step(pool, q, k, v, g, b, o, src_t if first else dst_t, dst_t)
+
+    for i in range(warmup):
+        step(steps + i, i == 0)
+    torch.cuda.synchronize()
+    storage.copy_(init)                       # timed run starts from the initial pool
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i, i == 0)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    span_ms = ev[0][0].elapsed_time(ev[-1][1])
+    per_req = decode_bytes_per_request(wl.HK, wl.HV, wl.dk, wl.dv, 2)
+    bytes_step = wl.B * per_req
+    value = bytes_step * steps / (span_ms * 1e-3) / 1e9
+    achieved = bytes_step / (launch_ms.mean() * 1e-3) / 1e9
+
+    # cold-cache figure: each launch preceded by a 1 GiB write (outside the events)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    cold = []
+    for i in range(min(steps, 20)):
+        flush.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step(i, False)
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+    cold_gbs = bytes_step / (float(np.median(cold)) * 1e-3) / 1e9
+    traffic = _traffic("decode_counters_batched_b64_h32_128x128.txt", ["gdn_decode.hip"], "hbm_bytes_per_launch")
+    pool.close()
+    return dict(
+        value=value, ms_per_step=span_ms / steps, wall_s=wall, achieved=achieved, cold_gbs=cold_gbs,
+        bytes_step=bytes_step, per_req=per_req, B=wl.B, HK=wl.HK, HV=wl.HV, dk=wl.dk, dv=wl.dv,
+        launch_ms_mean=float(launch_ms.mean()), traffic=traffic)
+
+
+def bench_prefill(reps=20, warmup=3):
+    import torch
+    from hybrid_linear_attention_02_amd import gdn
+    from hybrid_linear_attention_02_amd.workloads import chunked_prefill
+
+    pw = chunked_prefill()
+    tk = pw.tokens
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, g, b = bf(tk.q), bf(tk.k), bf(tk.v), dev(tk.g), dev(tk.beta)
+    T = int(pw.cu_seqlens[-1])
+    o = torch.empty((T, pw.HV, pw.dv), dtype=torch.bfloat16, device="cuda")
+    storage = torch.zeros((pw.num_slots, pw.HV, pw.dk, pw.dv), dtype=torch.float32, device="cuda")
+    pool = gdn.gdn_state_pool_create(pw.num_slots, pw.HV, pw.dk, pw.dv, storage=storage)
+    pool.alloc(pw.num_slots)
+    cu = dev(pw.cu_seqlens)
+    src = torch.tensor([-1], dtype=torch.int32, device="cuda")
+    dst = torch.tensor([1], dtype=torch.int32, device="cuda")
+    ws = None
+    for _ in range(warmup):
+        ws = gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src, dst, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src, dst, workspace=ws)
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(e))
+    t = float(np.median(times)) * 1e-3
+    flops = T * prefill_flops_per_token(pw.HV, pw.dk, pw.dv)
+    tflops = flops / t / 1e12
+    pool.close()
+    return {
+        "workload": "chunked_prefill_bf16_t8192_hk16_hv32_128x128_c64",
+        "value": T / t, "unit": "tok/s", "ms": t * 1e3, "dtype": "bf16",
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "scope": "whole gdn_prefill_chunked call (prep + intra-chunk + recurrence kernels)"},
+        "algorithmic_gflop": flops / 1e9,
+        "hbm_gbs_algorithmic": (T * prefill_bytes_per_token(pw.HK, pw.HV, pw.dk, pw.dv) + pw.HV * pw.dk * pw.dv * 4)
+        / t / 1e9,
+    }
+
+
+def _oracle_worker(args):
+    os.environ["OMP_NUM_THREADS"] = "1"
+    (pool_part, src, dst, steps_part, scale) = args
+    from oracle import bf16_bits_to_f64, decode_step
+    p = pool_part
+    t0 = time.perf_counter()
+    for i, (q, k, v, g, b) in enumerate(steps_part):
+        s = src if i == 0 else dst
+        _, p, _ = decode_step(p, s, dst, bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), g, b,
+                              scale, 1e-6)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(per_req_bytes, sample_requests=64, sample_steps=40):
+    """The fp64 oracle on a bounded sample of the decode workload: the first
+    `sample_requests` requests for `sample_steps` steps, one process per core
+    (up to the sample size), each process handling its own requests."""
+    from concurrent.futures import ProcessPoolExecutor
+    from hybrid_linear_attention_02_amd.workloads import batched_decode
+
+    wl = batched_decode(steps=sample_steps)
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16, sample_requests))
+    groups = np.array_split(np.arange(sample_requests), cores)
+    jobs = []
+    for gi, rows in enumerate(groups):
+        src = wl.src[rows]
+        # a private pool per worker: its sources plus fresh destination slots
+        npool = np.concatenate([wl.pool[src], np.zeros_like(wl.pool[src])])
+        lsrc = np.arange(len(rows))
+        ldst = np.arange(len(rows), 2 * len(rows))
+        steps_part = [(t.q[rows], t.k[rows], t.v[rows], t.g[rows], t.beta[rows]) for t in wl.steps]
+        jobs.append((npool, lsrc, ldst, steps_part, wl.dk ** -0.5))
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=cores) as ex:
+        list(ex.map(_oracle_worker, jobs))
+    wall = time.perf_counter() - t0
+    req_steps = sample_requests * sample_steps
+    return {"value": req_steps * per_req_bytes / wall / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"batched decode, first {sample_requests} of 64 requests x {sample_steps} steps "
+                      f"(fp64 token loop, {cores} processes); {req_steps / wall:.1f} request-steps/s, "
+                      f"wall {wall:.1f} s",
+            "request_steps_per_s": req_steps / wall}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the GDN state update shards over heads and requests with no "
+              "exchange, so there is no multi-GPU step to time here. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    # The CPU baseline forks its worker processes before this process touches
+    # the GPU.
+    cpu = None if args.no_cpu_baseline else cpu_baseline(decode_bytes_per_request(16, 32, 128, 128, 2))
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    from hybrid_linear_attention_02_amd import gdn
+    gdn.load_library()
+
+    d = bench_decode(args.steps, args.warmup)
+    pre = None if args.no_prefill else bench_prefill()
+    line = {
+        "metric": METRIC,
+        "value": round(d["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "batched_decode_bf16_b64_hk16_hv32_128x128_pool256",
+            "requests": d["B"], "k_heads": d["HK"], "v_heads": d["HV"], "dk": d["dk"], "dv": d["dv"],
+            "io_dtype": "bf16", "state_dtype": "f32", "pool_slots": 256,
+            "bytes_per_step": d["bytes_step"],
+        },
+        "hbm_frac": round(d["value"] / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm", "achieved": round(d["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(d["achieved"] / HBM_PEAK_GBS, 4), "traffic": d["traffic"],
+            "kernel": "gdn_decode_kernel<128,128,bf16>", "launch_us_mean": round(d["launch_ms_mean"] * 1e3, 2),
+        },
+        "cold_cache": {"value": round(d["cold_gbs"], 1), "unit": "GB/s", "frac": round(d["cold_gbs"] / HBM_PEAK_GBS, 4),
+                       "protocol": "median of 20 single launches, each after a 1 GiB device write"},
+        "cpu_baseline": cpu,
+        "prefill": pre,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

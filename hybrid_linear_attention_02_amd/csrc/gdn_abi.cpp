@@ -81,6 +81,7 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     if (!std::isfinite(a->scale) || !(a->l2_eps >= 0.0f) || !std::isfinite(a->l2_eps))
         return fail(GDN_E_INVALID, "gdn_prefill_chunked: scale must be finite and l2_eps finite and >= 0");
     const int32_t n = a->num_seqs;
+    if (n > 65535) return fail(GDN_E_INVALID, "gdn_prefill_chunked: at most 65535 sequences per call");
     int64_t chunks = 0;
     if (n > 0) {
         if (a->cu_seqlens_host == nullptr || a->cu_seqlens == nullptr)
