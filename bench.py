@@ -199,46 +199,56 @@ def bench_prefill(reps=20, warmup=3):
 
 def _oracle_worker(args):
     os.environ["OMP_NUM_THREADS"] = "1"
-    (pool_part, src, dst, steps_part, scale) = args
+    (pool_part, src, dst, steps_part, scale, repeats) = args
     from oracle import bf16_bits_to_f64, decode_step
-    p = pool_part
     t0 = time.perf_counter()
-    for i, (q, k, v, g, b) in enumerate(steps_part):
-        s = src if i == 0 else dst
-        _, p, _ = decode_step(p, s, dst, bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), g, b,
-                              scale, 1e-6)
+    for _ in range(repeats):
+        p = pool_part
+        for i, (q, k, v, g, b) in enumerate(steps_part):
+            s = src if i == 0 else dst
+            _, p, _ = decode_step(p, s, dst, bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v), g, b,
+                                  scale, 1e-6)
     return time.perf_counter() - t0
 
 
-def cpu_baseline(per_req_bytes, sample_requests=64, sample_steps=40):
-    """The fp64 oracle on a bounded sample of the decode workload: the first
-    `sample_requests` requests for `sample_steps` steps, one process per core
-    (up to the sample size), each process handling its own requests."""
+def cpu_baseline(per_req_bytes, repeats=4):
+    """The fp64 oracle (as it stands) on the whole batched-decode workload --
+    64 requests x 100 steps, run `repeats` times back to back so the timed CPU
+    work lasts some seconds -- one process per host core (at most 16), each
+    owning a contiguous block of requests and a private copy of their slots."""
     from concurrent.futures import ProcessPoolExecutor
     from hybrid_linear_attention_02_amd.workloads import batched_decode
 
-    wl = batched_decode(steps=sample_steps)
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16, sample_requests))
-    groups = np.array_split(np.arange(sample_requests), cores)
+    wl = batched_decode(steps=100)
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16, wl.B))
+    groups = np.array_split(np.arange(wl.B), cores)
     jobs = []
-    for gi, rows in enumerate(groups):
+    for rows in groups:
         src = wl.src[rows]
-        # a private pool per worker: its sources plus fresh destination slots
         npool = np.concatenate([wl.pool[src], np.zeros_like(wl.pool[src])])
         lsrc = np.arange(len(rows))
         ldst = np.arange(len(rows), 2 * len(rows))
         steps_part = [(t.q[rows], t.k[rows], t.v[rows], t.g[rows], t.beta[rows]) for t in wl.steps]
-        jobs.append((npool, lsrc, ldst, steps_part, wl.dk ** -0.5))
+        jobs.append((npool, lsrc, ldst, steps_part, wl.dk ** -0.5, repeats))
     t0 = time.perf_counter()
     with ProcessPoolExecutor(max_workers=cores) as ex:
         list(ex.map(_oracle_worker, jobs))
     wall = time.perf_counter() - t0
-    req_steps = sample_requests * sample_steps
+    req_steps = wl.B * len(wl.steps) * repeats
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": req_steps * per_req_bytes / wall / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"batched decode, first {sample_requests} of 64 requests x {sample_steps} steps "
-                      f"(fp64 token loop, {cores} processes); {req_steps / wall:.1f} request-steps/s, "
-                      f"wall {wall:.1f} s",
-            "request_steps_per_s": req_steps / wall}
+            "sample": f"whole batched-decode workload (64 requests x 100 steps, 16/32 heads, 128x128) run "
+                      f"{repeats} times; fp64 token loop in {cores} processes on {cpu_model or 'host CPU'}; "
+                      f"{req_steps / wall:.1f} request-steps/s, wall {wall:.1f} s",
+            "request_steps_per_s": req_steps / wall, "wall_s": wall}
 
 
 def main():
