@@ -104,8 +104,6 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     size_t off = 0;
     plan->off_chunk_offsets = off;
     off = up(off + sizeof(int32_t) * static_cast<size_t>(n + 1));
-    plan->off_kt = off;
-    off = up(off + 2ull * chunks * a->num_k_heads * a->dk * 64);
     plan->off_tp = off;
     off = up(off + 2ull * chunks * a->num_v_heads * 2 * 64 * 64);
     plan->off_sc = off;

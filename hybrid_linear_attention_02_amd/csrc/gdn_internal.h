@@ -31,9 +31,8 @@ int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream);
 struct PrefillPlan {
     int32_t num_chunks = 0;       // sum over sequences of ceil(len / 64)
     size_t off_chunk_offsets = 0; // int32 [N+1]: first chunk index of each sequence
-    size_t off_kt = 0;            // bf16 [chunks][HK][dk][64]: K^T per chunk
     size_t off_tp = 0;            // bf16 [chunks][HV][2][64][64]: T and P
-    size_t off_sc = 0;            // float [chunks][HV][4][64] + gamma_last
+    size_t off_sc = 0;            // float [chunks][HV][5][64]: per-token scale rows
     size_t bytes = 0;
 };
 int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* plan);

@@ -13,22 +13,27 @@
 //   O      = diag(exp(gamma)) Q~ H + P U
 //   H'     = exp(gamma_last) H + K^T diag(exp(gamma_last - gamma)) U
 //
-// (the WY / UT form: U = U' - W H with W = T diag(beta exp(gamma)) K^ and
-// U' = T diag(beta) V, here applied as T times one bracket). Decay factors are
-// always exp of a non-positive difference.
+// (the WY / UT form of the delta rule, applied as T times one bracket). Decay
+// factors are always exp of a non-positive difference.
 //
-// Two kernels after a tiny chunk-offset prep:
-//  * intra-chunk, one wave per (chunk, value head), fully parallel: row norms,
-//    the Gram matrices K K^T and Q K^T on bf16 MFMA (exact bf16 products, fp32
-//    accumulation), A staged in LDS, T by forward substitution in fp32 with
-//    the column in registers, and P, T, per-token scale factors and a
-//    transposed copy of the raw K tile written to the workspace;
+// Kernels, after a tiny chunk-offset prep:
+//  * intra-chunk, one wave per (chunk, value head), all chunks in parallel:
+//    the raw q / k rows of the chunk are held in registers in MFMA operand
+//    layout, row norms and the Gram matrices K K^T and Q K^T come from them
+//    on 16x16x32 bf16 MFMA, A goes to LDS (column-major), and T is solved in
+//    fp32 by a right-looking substitution (lane = column of T; each step
+//    broadcasts one column of A and updates every later row, so the serial
+//    chain is one FMA per row). T, P and five per-token scale rows go to the
+//    workspace.
 //  * recurrence, one workgroup per (sequence, value head, 16*NW value
-//    columns), sequential over the chunks of its sequence: each wave keeps
-//    its 16 columns of the fp32 master state in MFMA accumulators and runs
-//    X = K H, Z = Q H, U = T Y, O = scale Z + P U and H' = e H + K^T (D U) as
-//    bf16 MFMA contractions (16x16x32), with the chunk's operands staged
-//    through LDS. MFMA operands are bf16; accumulators and the state are fp32.
+//    columns), sequential over the chunks of its sequence. The fp32 master
+//    state lives in MFMA accumulators; X = K H, Z = Q H, U = T Y,
+//    O = diag(.) Z + P U and H' = e H + K^T (D U) are bf16 MFMA contractions.
+//    K^T and V are read transposed straight from the row-major LDS tiles with
+//    the gfx950 LDS transpose read, so no transposed copy is ever stored. The
+//    next chunk's operands are fetched into registers while the current chunk
+//    is computed (one LDS buffer, two barriers per chunk), and the output tile
+//    is staged in LDS and written with 16-byte stores.
 //
 // Raw (unnormalised) bf16 q and k are the MFMA operands; the L2 norms and the
 // decay factors are applied as fp32 row scales on the accumulator side.
@@ -46,9 +51,20 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kC = 64;        // chunk length
-constexpr int kScStride = 5;  // per-token scale rows in the workspace
+constexpr int kScRows = 5;    // per-token scale rows in the workspace
+
+// Rows of the per-(chunk, head) scale block.
+enum : int {
+    kScX = 0,     // exp(gamma_r) rk_r            scales X = K H
+    kScBeta = 1,  // beta_r
+    kScZ = 2,     // exp(gamma_r) rq_r            scales Z = Q H
+    kScD = 3,     // rk_r exp(gamma_last - gamma_r)  scales U in the state advance
+    kScE = 4,     // exp(gamma_last)              (every entry)
+};
 
 struct PrefillParams {
     const int32_t* cu;          // [N+1] device
@@ -63,9 +79,8 @@ struct PrefillParams {
     const int32_t* src;
     const int32_t* dst;
     int32_t* err;
-    uint16_t* kt;               // [chunks][HK][DK][64]   raw K^T per chunk
     uint16_t* tp;               // [chunks][HV][2][64][64] T then P
-    float* sc;                  // [chunks][HV][5][64]    scale factors
+    float* sc;                  // [chunks][HV][5][64]    scale rows
     int32_t* chunk_off_w;       // same buffer as chunk_off, written by the prep kernel
     int32_t n_seqs;
     int32_t num_chunks;
@@ -81,15 +96,17 @@ struct PrefillParams {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
-}
+// float -> bfloat16, round to nearest even, on the gfx950 packed convert
+// (v_cvt_pk_bf16_f32); NaN stays NaN.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
@@ -108,15 +125,78 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// MFMA operand read from a row-major bf16 LDS tile with the K-slot order that
-// matches an accumulator pair: slots 0-3 hold columns base+4g..+3 and slots
-// 4-7 columns base+16+4g..+3 (g = lane / 16). An fp32 accumulator tile pair
-// (rows base..base+15, base+16..base+31) packed with pack8 has exactly this
-// order, so either side can feed the other without a shuffle.
-__device__ __forceinline__ bf16x8 lds_pair(const uint16_t* buf, int stride, int row, int base, int g4) {
-    const uint16_t* p = buf + row * stride + base + 4 * g4;
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
+// K-slot convention shared by every operand below: inside a 32-wide k block,
+// slot e (e < 4) of lane group g = lane / 16 is k = 4g + e and slot 4 + e is
+// k = 16 + 4g + e. An fp32 accumulator pair (rows base..base+15 and
+// base+16..base+31, lane = column, 4 rows 4g..4g+3 per lane) packed with
+// pack8 has exactly this order, so results feed the next contraction
+// directly.
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane j receives element (j & 3) of the 4 consecutive 16-bit values loaded
+// by lanes 4e + (j >> 2), for e = 0..3. Pointing lane i of group g at
+// M[row0 + 4g + (i >> 2)][col0 + 4 (i & 3)] therefore hands lane (g, j) the
+// column values M[row0 + 4g + e][col0 + j], e = 0..3.
+__device__ __forceinline__ i16x4 lds_tr4_raw(const uint16_t* buf, int stride, int row0, int col0, int g4, int l16) {
+    const uint16_t* a = buf + (row0 + 4 * g4 + (l16 >> 2)) * stride + col0 + 4 * (l16 & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a));
+}
+
+// M[row0 + 4g + e][col0 + lane % 16] for e = 0..3 as fp32: a column slice in
+// accumulator layout.
+__device__ __forceinline__ f32x4 lds_tr4_f32(const uint16_t* buf, int stride, int row0, int col0, int g4, int l16) {
+    const i16x4 r = lds_tr4_raw(buf, stride, row0, col0, g4, l16);
+    f32x4 out;
+    out.x = bf16_to_f32(static_cast<uint16_t>(r.x));
+    out.y = bf16_to_f32(static_cast<uint16_t>(r.y));
+    out.z = bf16_to_f32(static_cast<uint16_t>(r.z));
+    out.w = bf16_to_f32(static_cast<uint16_t>(r.w));
+    return out;
+}
+
+// LDS bank model behind the layouts below (measured on gfx950 with the
+// SQ_LDS_BANK_CONFLICT counter): 64 banks of 4 bytes; a single 8-byte-per-lane
+// read is served 32 lanes per pass and is conflict-free when those lanes'
+// 64 dwords sit in distinct banks. When the compiler fuses two such reads
+// into one two-address instruction, that instruction costs extra cycles even
+// if each half alone would be conflict-free; so every layout below also makes
+// the address difference between any two operand reads depend on the lane,
+// which the compiler cannot fuse.
+//
+// Tiles are stored with unpadded rows of G 8-byte granules, and granule j of
+// row r sits at granule j ^ swz(r), where swz(r) is even (16-byte pairs stay
+// aligned and contiguous, so 16-byte staging writes are unchanged) and is the
+// XOR of a per-row term and a per-16-row-group constant that also differs
+// between tiles of the same shape.
+
+// q/k tiles (64 rows x DK bf16), read as MFMA row operands (16 rows x 2
+// granules per pass) and through the transpose read (8 consecutive rows x 4
+// consecutive granules per pass). Per-row term 4 ((r >> a) & m) +
+// 2 ((r >> 3) & 1), with a = log2(32 / G) and m = G / 4 - 1: the 16 rows of a
+// row-operand read get 16 distinct granule offsets (2 ... 32 / G rows share
+// one pass of banks), the 8 rows of a transpose read differ above the
+// 4-granule span. Group constant 2 (r >> 4), plus 8 for the q tile.
+template <int DK, bool IS_Q>
+__device__ __forceinline__ int kq_swz(int r) {
+    constexpr int G = DK / 4;
+    constexpr int A = (G == 32) ? 0 : (G == 16) ? 1 : 2;
+    constexpr int M = G / 4 - 1;
+    static_assert(G == 8 || G == 16 || G == 32, "dk must be 32, 64 or 128");
+    const int group = (2 * (r >> 4) + (IS_Q ? 8 : 0)) & (G - 2);
+    return (4 * ((r >> A) & M) + 2 * ((r >> 3) & 1)) ^ group;
+}
+
+// element offset of (row r, column col) in a swizzled q/k tile; col % 4 == 0
+template <int DK, bool IS_Q>
+__device__ __forceinline__ int kq_off(int r, int col) {
+    return r * DK + 4 * ((col >> 2) ^ kq_swz<DK, IS_Q>(r)) + (col & 3);
+}
+
+// Row operand from a swizzled q/k tile: slots = M[row][base + k(slot)].
+template <int DK, bool IS_Q>
+__device__ __forceinline__ bf16x8 kq_pair(const uint16_t* buf, int row, int base, int g4) {
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(buf + kq_off<DK, IS_Q>(row, base + 4 * g4));
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(buf + kq_off<DK, IS_Q>(row, base + 16 + 4 * g4));
     u32x4 w;
     w.x = lo.x;
     w.y = lo.y;
@@ -125,9 +205,54 @@ __device__ __forceinline__ bf16x8 lds_pair(const uint16_t* buf, int stride, int 
     return as_bf16x8(w);
 }
 
-// 8 consecutive bf16 (contiguous K-slot order).
-__device__ __forceinline__ bf16x8 lds_row8(const uint16_t* buf, int stride, int row, int base) {
-    return as_bf16x8(*reinterpret_cast<const u32x4*>(buf + row * stride + base));
+// Transposed operand from a swizzled k tile: slots = M[row0 + k(slot)][col0 + lane % 16].
+template <int DK>
+__device__ __forceinline__ bf16x8 kq_tr_pair(const uint16_t* buf, int row0, int col0, int g4, int l16) {
+    const int r = row0 + 4 * g4 + (l16 >> 2);
+    const int c = col0 + 4 * (l16 & 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + kq_off<DK, false>(r, c)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + kq_off<DK, false>(r + 16, c)));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+    u32x4 w;
+    w.x = l2.x;
+    w.y = l2.y;
+    w.z = h2.x;
+    w.w = h2.y;
+    return as_bf16x8(w);
+}
+
+// T and P tiles (64 x 64 bf16, G = 16), read only as row operands. A row
+// fills half of the banks, so the 8 same-parity rows of a pass need distinct
+// granule offsets: per-row term 2 ((r >> 1) & 7). Group constant 2 (r >> 4),
+// plus 8 for P.
+template <bool IS_P>
+__device__ __forceinline__ int tp_off(int r, int col) {
+    const int swz = (2 * ((r >> 1) & 7)) ^ ((2 * (r >> 4) + (IS_P ? 8 : 0)) & 14);
+    return r * kC + 4 * ((col >> 2) ^ swz) + (col & 3);
+}
+
+template <bool IS_P>
+__device__ __forceinline__ bf16x8 tp_pair(const uint16_t* buf, int row, int base, int g4) {
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(buf + tp_off<IS_P>(row, base + 4 * g4));
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(buf + tp_off<IS_P>(row, base + 16 + 4 * g4));
+    u32x4 w;
+    w.x = lo.x;
+    w.y = lo.y;
+    w.z = hi.x;
+    w.w = hi.y;
+    return as_bf16x8(w);
+}
+
+// Workgroup barrier that orders LDS only. A plain __syncthreads() also waits
+// for every outstanding global load and store of the wave (the workgroup
+// release fence covers global memory), which would put a full memory round
+// trip on every chunk; the kernels here exchange data between waves through
+// LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---------------------------------------------------------------------------
@@ -163,11 +288,8 @@ __device__ __forceinline__ int find_seq(const int32_t* off, int n_seqs, int c) {
 template <int DK>
 __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     constexpr int KS = DK / 32;       // MFMA k-steps over dk
-    constexpr int SK = DK + 8;        // LDS row stride of the q/k tiles (bf16)
-    constexpr int SA = kC + 4;        // LDS row stride of A (fp32)
-    __shared__ __align__(16) uint16_t sK[kC * SK];
-    __shared__ __align__(16) uint16_t sQ[kC * SK];
-    __shared__ __align__(16) float sA[kC * SA];
+    constexpr int SA = kC + 4;        // row stride of A^T in LDS (fp32)
+    __shared__ __align__(16) float sAt[kC * SA];   // sAt[s][r] = A[r][s]
     __shared__ float sGam[kC], sBeta[kC], sRk[kC], sRq[kC];
 
     const int c = blockIdx.x;
@@ -182,17 +304,22 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     if (len <= 0 || tend > p.total_tokens || p.dst[n] < 0) return;
     const int j = h / p.group;
 
-    // stage the raw q / k rows of the chunk (zero rows past the end)
-    for (int idx = lane; idx < kC * (DK / 8); idx += 64) {
-        const int r = idx / (DK / 8), c8 = idx % (DK / 8);
-        u32x4 kv = u32x4{0u, 0u, 0u, 0u}, qv = u32x4{0u, 0u, 0u, 0u};
-        if (r < len) {
-            const size_t off = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + c8 * 8;
-            kv = *reinterpret_cast<const u32x4*>(p.k + off);
-            qv = *reinterpret_cast<const u32x4*>(p.q + off);
+    // raw q / k rows in operand layout: xr[tt][ks] = X[16 tt + l16][32 ks + 8 g .. +7]
+    u32x4 kr[4][KS], qr[4][KS];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int r = 16 * tt + l16;
+        const size_t base = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (r < len) {
+                kr[tt][ks] = *reinterpret_cast<const u32x4*>(p.k + base + 32 * ks);
+                qr[tt][ks] = *reinterpret_cast<const u32x4*>(p.q + base + 32 * ks);
+            } else {
+                kr[tt][ks] = u32x4{0u, 0u, 0u, 0u};
+                qr[tt][ks] = u32x4{0u, 0u, 0u, 0u};
+            }
         }
-        *reinterpret_cast<u32x4*>(sK + r * SK + c8 * 8) = kv;
-        *reinterpret_cast<u32x4*>(sQ + r * SK + c8 * 8) = qv;
     }
     // per-token g, beta; cumulative log-decay by an inclusive lane scan
     float gl = 0.f, bl = 0.f;
@@ -208,42 +335,51 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         if (lane >= off) gam += t;
     }
     const float gam_last = __shfl(gam, 63);   // padded tokens add g = 0
-    __syncthreads();
-
-    // L2 norms of row `lane` (fp32 sums of exact bf16 squares)
-    float sk = 0.f, sq = 0.f;
-    for (int d8 = 0; d8 < DK / 8; ++d8) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(sK + lane * SK + d8 * 8);
-        const u32x4 qv = *reinterpret_cast<const u32x4*>(sQ + lane * SK + d8 * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float k0 = __uint_as_float(kv[e] << 16), k1 = __uint_as_float(kv[e] & 0xffff0000u);
-            const float q0 = __uint_as_float(qv[e] << 16), q1 = __uint_as_float(qv[e] & 0xffff0000u);
-            sk += k0 * k0 + k1 * k1;
-            sq += q0 * q0 + q1 * q1;
-        }
-    }
-    const bool live = lane < len;
-    const float rk = live ? 1.0f / sqrtf(sk + p.eps) : 0.f;
-    const float rq = live ? p.scale / sqrtf(sq + p.eps) : 0.f;
     sGam[lane] = gam;
     sBeta[lane] = bl;
-    sRk[lane] = rk;
-    sRq[lane] = rq;
-    {
-        float* scp = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScStride * kC);
-        const float eg = expf(gam);
-        scp[0 * kC + lane] = eg * rk;                      // row scale of K H
-        scp[1 * kC + lane] = bl;                           // beta
-        scp[2 * kC + lane] = eg * rq;                      // row scale of Q H
-        scp[3 * kC + lane] = rk * expf(gam_last - gam);    // row scale of U in the state advance
-        scp[4 * kC + lane] = expf(gam_last);               // state decay over the chunk
-    }
-    __syncthreads();
 
-    // Gram matrices on MFMA, lower-triangular 16x16 tiles; A -> LDS, P -> global
+    // L2 norms of rows 16 tt + l16 (fp32 sums of exact bf16 squares)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float k0 = __uint_as_float(kr[tt][ks][e] << 16), k1 = __uint_as_float(kr[tt][ks][e] & 0xffff0000u);
+                const float q0 = __uint_as_float(qr[tt][ks][e] << 16), q1 = __uint_as_float(qr[tt][ks][e] & 0xffff0000u);
+                sk += k0 * k0 + k1 * k1;
+                sq += q0 * q0 + q1 * q1;
+            }
+        }
+        sk += __shfl_xor(sk, 16);
+        sq += __shfl_xor(sq, 16);
+        sk += __shfl_xor(sk, 32);
+        sq += __shfl_xor(sq, 32);
+        const int r = 16 * tt + l16;
+        if (g4 == 0) {
+            const bool live = r < len;
+            sRk[r] = live ? 1.0f / sqrtf(sk + p.eps) : 0.f;
+            sRq[r] = live ? p.scale / sqrtf(sq + p.eps) : 0.f;
+        }
+    }
+    lds_barrier();
+    {
+        const float rk = sRk[lane], rq = sRq[lane];
+        const float eg = expf(gam);
+        float* scp = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScRows * kC);
+        scp[kScX * kC + lane] = eg * rk;
+        scp[kScBeta * kC + lane] = bl;
+        scp[kScZ * kC + lane] = eg * rq;
+        scp[kScD * kC + lane] = rk * expf(gam_last - gam);
+        scp[kScE * kC + lane] = expf(gam_last);
+    }
+
+    // Gram tiles on MFMA: A (strictly lower) -> LDS transposed, P -> workspace.
     uint16_t* Pg = p.tp + ((static_cast<size_t>(c) * p.hv + h) * 2 + 1) * (kC * kC);
+#pragma unroll
     for (int tr = 0; tr < 4; ++tr) {
+#pragma unroll
         for (int ts = 0; ts < 4; ++ts) {
             if (ts > tr) {
 #pragma unroll
@@ -253,55 +389,52 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
             f32x4 kk = f32x4{0.f, 0.f, 0.f, 0.f}, qk = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 ak = lds_row8(sK, SK, 16 * tr + l16, 32 * ks + 8 * g4);
-                const bf16x8 aq = lds_row8(sQ, SK, 16 * tr + l16, 32 * ks + 8 * g4);
-                const bf16x8 bk = lds_row8(sK, SK, 16 * ts + l16, 32 * ks + 8 * g4);
-                kk = mfma16(ak, bk, kk);
-                qk = mfma16(aq, bk, qk);
+                const bf16x8 bk = as_bf16x8(kr[ts][ks]);
+                kk = mfma16(as_bf16x8(kr[tr][ks]), bk, kk);
+                qk = mfma16(as_bf16x8(qr[tr][ks]), bk, qk);
             }
             const int s = 16 * ts + l16;
+            const float gs = sGam[s], rks = sRk[s];
+            f32x4 a;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * tr + 4 * g4 + i;
-                const float dec = (s <= r) ? expf(sGam[r] - sGam[s]) : 0.f;
-                sA[r * SA + s] = (s < r) ? sBeta[r] * dec * kk[i] * sRk[r] * sRk[s] : 0.f;
-                Pg[r * kC + s] = f32_to_bf16(dec * qk[i] * sRq[r] * sRk[s]);
+                const float dec = (s <= r) ? expf(sGam[r] - gs) : 0.f;
+                a[i] = (s < r) ? sBeta[r] * dec * kk[i] * sRk[r] * rks : 0.f;
+                Pg[r * kC + s] = f32_to_bf16(dec * qk[i] * sRq[r] * rks);
             }
+            *reinterpret_cast<f32x4*>(sAt + s * SA + 16 * tr + 4 * g4) = a;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // T = (I + A)^-1 by forward substitution; lane t owns column t (rows
-    // above t come out zero). A row r is read as float4s; its entries at
-    // s >= r are zero inside the diagonal tile, and tc[s >= r] is still zero.
-    // The address of row r is made to depend on tc[r - 2] through an empty
-    // asm, so at most two rows of A are in registers at a time (otherwise the
-    // scheduler hoists all 2016 loads and spills).
-    float tc[kC];
+    // T = (I + A)^-1, right-looking: lane t owns column t of T. Step s fixes
+    // x_s and adds A[r][s] x_s to every later row r; only x_s's own update is
+    // on the serial chain. The address of column s of A is tied to x_{s-2}
+    // through an empty asm so at most two columns are in flight (otherwise
+    // the scheduler hoists every load and spills).
+    float x[kC];
 #pragma unroll
-    for (int r = 0; r < kC; ++r) tc[r] = 0.f;
+    for (int r = 0; r < kC; ++r) x[r] = 0.f;
 #pragma unroll
-    for (int r = 0; r < kC; ++r) {
-        int row_off = r * SA;
-        if (r >= 2) __asm__ volatile("" : "+v"(row_off) : "v"(tc[r - 2]));
-        const float* arow = sA + row_off;
-        float acc = 0.f;
+    for (int s = 0; s < kC; ++s) {
+        x[s] = ((s == lane) ? 1.f : 0.f) - x[s];
+        if (s == kC - 1) break;
+        int col_off = s * SA;
+        if (s >= 2) __asm__ volatile("" : "+v"(col_off) : "v"(x[s - 2]));
+        const float* acol = sAt + col_off;
+        const float xs = x[s];
 #pragma unroll
-        for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(arow + 4 * q4);
-            acc += a.x * tc[4 * q4] + a.y * tc[4 * q4 + 1] + a.z * tc[4 * q4 + 2] + a.w * tc[4 * q4 + 3];
+        for (int r4 = (s + 1) / 4; r4 < kC / 4; ++r4) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(acol + 4 * r4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * r4 + e > s) x[4 * r4 + e] += a[e] * xs;
         }
-        tc[r] = (r == lane) ? 1.f : -acc;
     }
     uint16_t* Tg = p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC);
 #pragma unroll
-    for (int r = 0; r < kC; ++r) Tg[r * kC + lane] = f32_to_bf16(tc[r]);
-
-    // raw K^T of the chunk, once per key head
-    if (h % p.group == 0) {
-        uint16_t* Ktg = p.kt + (static_cast<size_t>(c) * p.hk + j) * (DK * kC);
-        for (int d = 0; d < DK; ++d) Ktg[d * kC + lane] = sK[lane * SK + d];
-    }
+    for (int r = 0; r < kC; ++r) Tg[r * kC + lane] = f32_to_bf16(x[r]);
 }
 
 // ---------------------------------------------------------------------------
@@ -309,30 +442,53 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
 // ---------------------------------------------------------------------------
 
 template <int DK, int NW>
-__global__ void __launch_bounds__(64 * NW) prefill_recurrent_kernel(PrefillParams p) {
-    constexpr int KS = DK / 32;       // k-steps over dk
-    constexpr int MT = DK / 16;       // 16-row tiles of the state
-    constexpr int SK = DK + 8;        // q/k tile row stride (bf16)
-    constexpr int ST = kC + 8;        // K^T, T, P row stride (bf16)
-    constexpr int NV = 16 * NW;       // value columns per workgroup
-    constexpr int SV = NV + 8;        // v tile row stride (bf16)
-    constexpr int NT = 64 * NW;
-    __shared__ __align__(16) uint16_t sK[kC * SK];
-    __shared__ __align__(16) uint16_t sQ[kC * SK];
-    __shared__ __align__(16) uint16_t sKt[DK * ST];
-    __shared__ __align__(16) uint16_t sT[kC * ST];
-    __shared__ __align__(16) uint16_t sP[kC * ST];
+struct RecShape {
+    static constexpr int NT = 64 * NW;        // threads
+    static constexpr int NV = 16 * NW;        // value columns per workgroup
+    static constexpr int KS = DK / 32;        // k-steps over dk
+    static constexpr int MT = DK / 16;        // 16-row tiles of the state
+    static constexpr int SV = NV + 16;        // bf16 row strides of the padded tiles (bank note below)
+    static constexpr int SO = NV + 8;
+    static constexpr int KQ = 8 * DK / NT;    // 16-byte pieces per thread: K (and Q) tile
+    static constexpr int TP = 512 / NT;       //                            T (and P) tile
+    static constexpr int VV = 8 * NV / NT;    //                            V tile slice
+    static constexpr int SCN = (kScRows * kC / 4 + NT - 1) / NT;   // scale rows
+    static_assert(KQ * NT == 8 * DK && TP * NT == 512 && VV * NT == 8 * NV, "tile split");
+};
+// Bank note (same model as for the swizzled tiles): V is read only through
+// the transpose read, 8 rows x 4 granules per pass; a stride of 4 granules
+// more than the tile width (20 granules at 64 columns) spaces those rows 4 or
+// more granules apart. The output staging tile is written 2 bytes per lane (4
+// rows x 16 columns per instruction) and read back 16 bytes per lane; a
+// stride of 2 granules more than the width keeps both near conflict-free.
+
+template <int DK, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+prefill_recurrent_kernel(PrefillParams p) {
+    using S = RecShape<DK, NW>;
+    constexpr int NT = S::NT, NV = S::NV, KS = S::KS, MT = S::MT;
+    constexpr int SV = S::SV, SO = S::SO;
+    constexpr int KQ = S::KQ, TP = S::TP, VV = S::VV, SCN = S::SCN;
+    __shared__ __align__(16) uint16_t sK[kC * DK];   // swizzled, see kq_swz
+    __shared__ __align__(16) uint16_t sQ[kC * DK];
+    __shared__ __align__(16) uint16_t sT[kC * kC];   // swizzled, see tp_off
+    __shared__ __align__(16) uint16_t sP[kC * kC];
     __shared__ __align__(16) uint16_t sV[kC * SV];
-    __shared__ __align__(16) float sSc[kScStride * kC];
+    __shared__ __align__(16) uint16_t sO[kC * SO];
+    __shared__ __align__(16) float sSc[kScRows * kC];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g4 = lane >> 4, l16 = lane & 15;
-    const int groups = p.dv / NV;
-    const int h = blockIdx.x / groups;
-    const int grp = blockIdx.x - h * groups;
+    // blockIdx.x -> (key head, value head in its group, column group), key
+    // head fastest so that the workgroups sharing one key head's q/k rows sit
+    // on the same XCD (workgroups are dealt to the 8 XCDs round robin).
+    const int j = blockIdx.x % p.hk;
+    const int rest = blockIdx.x / p.hk;
+    const int hig = rest % p.group;
+    const int grp = rest / p.group;
+    const int h = j * p.group + hig;
     const int n = blockIdx.y;
-    const int j = h / p.group;
 
     const int dsl = p.dst[n];
     if (dsl < 0) return;
@@ -359,108 +515,182 @@ __global__ void __launch_bounds__(64 * NW) prefill_recurrent_kernel(PrefillParam
         for (int mu = 0; mu < MT; ++mu) H[mu] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // register staging of one chunk's operands (the next chunk is fetched
+    // while the current one is computed)
+    u32x4 rK[KQ], rQ[KQ], rT[TP], rP[TP], rV[VV], rS[SCN];
+    auto fetch = [&](int c) {
+        const int t0 = tb + (c - c0) * kC;
+        const int len = min(kC, te - t0);
+#pragma unroll
+        for (int m = 0; m < KQ; ++m) {
+            const int idx = tid + NT * m;
+            const int r = idx / (DK / 8), c8 = idx % (DK / 8);
+            if (r < len) {
+                const size_t off = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + c8 * 8;
+                rK[m] = *reinterpret_cast<const u32x4*>(p.k + off);
+                rQ[m] = *reinterpret_cast<const u32x4*>(p.q + off);
+            } else {
+                rK[m] = u32x4{0u, 0u, 0u, 0u};
+                rQ[m] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        const uint16_t* TPg = p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC);
+#pragma unroll
+        for (int m = 0; m < TP; ++m) {
+            const int idx = tid + NT * m;
+            rT[m] = *reinterpret_cast<const u32x4*>(TPg + 8 * idx);
+            rP[m] = *reinterpret_cast<const u32x4*>(TPg + kC * kC + 8 * idx);
+        }
+#pragma unroll
+        for (int m = 0; m < VV; ++m) {
+            const int idx = tid + NT * m;
+            const int r = idx / (NV / 8), c8 = idx % (NV / 8);
+            rV[m] = u32x4{0u, 0u, 0u, 0u};
+            if (r < len)
+                rV[m] = *reinterpret_cast<const u32x4*>(p.v + (static_cast<size_t>(t0 + r) * p.hv + h) * p.dv + vcol0 + 8 * c8);
+        }
+        const float* SCg = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScRows * kC);
+#pragma unroll
+        for (int m = 0; m < SCN; ++m) {
+            const int idx = tid + NT * m;
+            if (idx < kScRows * kC / 4) rS[m] = *reinterpret_cast<const u32x4*>(SCg + 4 * idx);
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int m = 0; m < KQ; ++m) {
+            const int idx = tid + NT * m;
+            const int r = idx / (DK / 8), c8 = idx % (DK / 8);
+            *reinterpret_cast<u32x4*>(sK + kq_off<DK, false>(r, c8 * 8)) = rK[m];
+            *reinterpret_cast<u32x4*>(sQ + kq_off<DK, true>(r, c8 * 8)) = rQ[m];
+        }
+#pragma unroll
+        for (int m = 0; m < TP; ++m) {
+            const int idx = tid + NT * m;
+            const int r = idx / 8, c8 = idx % 8;
+            *reinterpret_cast<u32x4*>(sT + tp_off<false>(r, c8 * 8)) = rT[m];
+            *reinterpret_cast<u32x4*>(sP + tp_off<true>(r, c8 * 8)) = rP[m];
+        }
+#pragma unroll
+        for (int m = 0; m < VV; ++m) {
+            const int idx = tid + NT * m;
+            const int r = idx / (NV / 8), c8 = idx % (NV / 8);
+            *reinterpret_cast<u32x4*>(sV + r * SV + c8 * 8) = rV[m];
+        }
+#pragma unroll
+        for (int m = 0; m < SCN; ++m) {
+            const int idx = tid + NT * m;
+            if (idx < kScRows * kC / 4) *reinterpret_cast<u32x4*>(sSc + 4 * idx) = rS[m];
+        }
+    };
+    // write the staged output tile of the chunk starting at token t0o
+    auto store_o = [&](int t0o, int leno) {
+#pragma unroll
+        for (int m = 0; m < VV; ++m) {
+            const int idx = tid + NT * m;
+            const int r = idx / (NV / 8), c8 = idx % (NV / 8);
+            if (r < leno)
+                *reinterpret_cast<u32x4*>(p.o + (static_cast<size_t>(t0o + r) * p.hv + h) * p.dv + vcol0 + 8 * c8) =
+                    *reinterpret_cast<const u32x4*>(sO + r * SO + c8 * 8);
+        }
+    };
+
+    if (c0 < c1) fetch(c0);
+    int prev_t0 = 0, prev_len = 0;
     for (int c = c0; c < c1; ++c) {
         const int t0 = tb + (c - c0) * kC;
         const int len = min(kC, te - t0);
-        __syncthreads();   // every wave is done with the previous chunk's tiles
-        for (int idx = tid; idx < kC * (DK / 8); idx += NT) {
-            const int r = idx / (DK / 8), c8 = idx % (DK / 8);
-            u32x4 kv = u32x4{0u, 0u, 0u, 0u}, qv = u32x4{0u, 0u, 0u, 0u};
-            if (r < len) {
-                const size_t off = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + c8 * 8;
-                kv = *reinterpret_cast<const u32x4*>(p.k + off);
-                qv = *reinterpret_cast<const u32x4*>(p.q + off);
-            }
-            *reinterpret_cast<u32x4*>(sK + r * SK + c8 * 8) = kv;
-            *reinterpret_cast<u32x4*>(sQ + r * SK + c8 * 8) = qv;
-        }
-        const uint16_t* Ktg = p.kt + (static_cast<size_t>(c) * p.hk + j) * (DK * kC);
-        for (int idx = tid; idx < DK * (kC / 8); idx += NT) {
-            const int d = idx / (kC / 8), c8 = idx % (kC / 8);
-            *reinterpret_cast<u32x4*>(sKt + d * ST + c8 * 8) = *reinterpret_cast<const u32x4*>(Ktg + d * kC + c8 * 8);
-        }
-        const uint16_t* TPg = p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC);
-        for (int idx = tid; idx < 2 * kC * (kC / 8); idx += NT) {
-            const int which = idx / (kC * kC / 8);
-            const int rem = idx - which * (kC * kC / 8);
-            const int r = rem / (kC / 8), c8 = rem % (kC / 8);
-            uint16_t* dstp = (which ? sP : sT) + r * ST + c8 * 8;
-            *reinterpret_cast<u32x4*>(dstp) = *reinterpret_cast<const u32x4*>(TPg + which * (kC * kC) + r * kC + c8 * 8);
-        }
-        for (int idx = tid; idx < kC * (NV / 8); idx += NT) {
-            const int r = idx / (NV / 8), c8 = idx % (NV / 8);
-            u32x4 vv = u32x4{0u, 0u, 0u, 0u};
-            if (r < len)
-                vv = *reinterpret_cast<const u32x4*>(p.v + (static_cast<size_t>(t0 + r) * p.hv + h) * p.dv + vcol0 + c8 * 8);
-            *reinterpret_cast<u32x4*>(sV + r * SV + c8 * 8) = vv;
-        }
-        const float* SCg = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScStride * kC);
-        for (int idx = tid; idx < kScStride * kC; idx += NT) sSc[idx] = SCg[idx];
-        __syncthreads();
+        lds_barrier();                 // previous chunk's LDS reads and sO writes are done
+        if (prev_len > 0) store_o(prev_t0, prev_len);
+        stage();
+        lds_barrier();
+        if (c + 1 < c1) fetch(c + 1);    // in flight while this chunk is computed
 
         // X = K H and Z = Q H  (contraction over dk)
         bf16x8 hb[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) hb[ks] = pack8(H[2 * ks], H[2 * ks + 1]);
+        // k-step outer, row tile inner: each step reads its 8 operands first and
+        // then issues 8 independent MFMAs, so LDS latency overlaps the matrix
+        // pipe instead of stalling every instruction.
         f32x4 X[4], Z[4];
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
             X[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
             Z[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                X[tau] = mfma16(lds_pair(sK, SK, 16 * tau + l16, 32 * ks, g4), hb[ks], X[tau]);
-                Z[tau] = mfma16(lds_pair(sQ, SK, 16 * tau + l16, 32 * ks, g4), hb[ks], Z[tau]);
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 ak[4], aq[4];
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+                ak[tau] = kq_pair<DK, false>(sK, 16 * tau + l16, 32 * ks, g4);
+                aq[tau] = kq_pair<DK, true>(sQ, 16 * tau + l16, 32 * ks, g4);
+            }
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+                X[tau] = mfma16(ak[tau], hb[ks], X[tau]);
+                Z[tau] = mfma16(aq[tau], hb[ks], Z[tau]);
             }
         }
         // Y = diag(beta) (V - diag(exp(gamma) rk) X)
         f32x4 Y[4];
 #pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * tau + 4 * g4 + i;
-                const float vv = bf16_to_f32(sV[r * SV + wave * 16 + l16]);
-                Y[tau][i] = sSc[kC + r] * (vv - sSc[r] * X[tau][i]);
-            }
+        for (int tau = 0; tau < 4; ++tau) {
+            const int r0 = 16 * tau + 4 * g4;
+            const f32x4 sx = *reinterpret_cast<const f32x4*>(sSc + kScX * kC + r0);
+            const f32x4 sb = *reinterpret_cast<const f32x4*>(sSc + kScBeta * kC + r0);
+            const f32x4 vv = lds_tr4_f32(sV, SV, 16 * tau, wave * 16, g4, l16);
+            Y[tau] = sb * (vv - sx * X[tau]);
+        }
         const bf16x8 yb0 = pack8(Y[0], Y[1]), yb1 = pack8(Y[2], Y[3]);
         // U = T Y   (T lower triangular: skip the all-zero upper k-step)
         f32x4 U[4];
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
-            U[tau] = mfma16(lds_pair(sT, ST, 16 * tau + l16, 0, g4), yb0, f32x4{0.f, 0.f, 0.f, 0.f});
-            if (tau >= 2) U[tau] = mfma16(lds_pair(sT, ST, 16 * tau + l16, 32, g4), yb1, U[tau]);
+            U[tau] = mfma16(tp_pair<false>(sT, 16 * tau + l16, 0, g4), yb0, f32x4{0.f, 0.f, 0.f, 0.f});
+            if (tau >= 2) U[tau] = mfma16(tp_pair<false>(sT, 16 * tau + l16, 32, g4), yb1, U[tau]);
         }
         const bf16x8 ub0 = pack8(U[0], U[1]), ub1 = pack8(U[2], U[3]);
-        // O = diag(exp(gamma) rq) Z + P U
+        // O = diag(exp(gamma) rq) Z + P U  -> staged in LDS as bf16
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
-            f32x4 O = mfma16(lds_pair(sP, ST, 16 * tau + l16, 0, g4), ub0, f32x4{0.f, 0.f, 0.f, 0.f});
-            if (tau >= 2) O = mfma16(lds_pair(sP, ST, 16 * tau + l16, 32, g4), ub1, O);
+            f32x4 O = mfma16(tp_pair<true>(sP, 16 * tau + l16, 0, g4), ub0, f32x4{0.f, 0.f, 0.f, 0.f});
+            if (tau >= 2) O = mfma16(tp_pair<true>(sP, 16 * tau + l16, 32, g4), ub1, O);
+            const int r0 = 16 * tau + 4 * g4;
+            const f32x4 sz = *reinterpret_cast<const f32x4*>(sSc + kScZ * kC + r0);
+            O += sz * Z[tau];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * tau + 4 * g4 + i;
-                if (r < len) {
-                    const float ov = sSc[2 * kC + r] * Z[tau][i] + O[i];
-                    p.o[(static_cast<size_t>(t0 + r) * p.hv + h) * p.dv + col] = f32_to_bf16(ov);
-                }
-            }
+            for (int i = 0; i < 4; ++i) sO[(r0 + i) * SO + wave * 16 + l16] = f32_to_bf16(O[i]);
         }
         // H' = exp(gamma_last) H + K^T diag(rk exp(gamma_last - gamma)) U
         f32x4 DU[4];
 #pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) DU[tau][i] = sSc[3 * kC + 16 * tau + 4 * g4 + i] * U[tau][i];
-        const bf16x8 db0 = pack8(DU[0], DU[1]), db1 = pack8(DU[2], DU[3]);
-        const float e = sSc[4 * kC];
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu) {
-            H[mu] *= e;
-            H[mu] = mfma16(lds_pair(sKt, ST, 16 * mu + l16, 0, g4), db0, H[mu]);
-            H[mu] = mfma16(lds_pair(sKt, ST, 16 * mu + l16, 32, g4), db1, H[mu]);
+        for (int tau = 0; tau < 4; ++tau) {
+            const f32x4 sd = *reinterpret_cast<const f32x4*>(sSc + kScD * kC + 16 * tau + 4 * g4);
+            DU[tau] = sd * U[tau];
         }
+        const bf16x8 db0 = pack8(DU[0], DU[1]), db1 = pack8(DU[2], DU[3]);
+        const float e = sSc[kScE * kC];
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu) H[mu] *= e;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const bf16x8 db = kt ? db1 : db0;
+#pragma unroll
+            for (int m0 = 0; m0 < MT; m0 += 4) {
+                bf16x8 at[4];
+#pragma unroll
+                for (int m = 0; m < 4 && m0 + m < MT; ++m) at[m] = kq_tr_pair<DK>(sK, 32 * kt, 16 * (m0 + m), g4, l16);
+#pragma unroll
+                for (int m = 0; m < 4 && m0 + m < MT; ++m) H[m0 + m] = mfma16(at[m], db, H[m0 + m]);
+            }
+        }
+        prev_t0 = t0;
+        prev_len = len;
     }
+    lds_barrier();
+    if (prev_len > 0) store_o(prev_t0, prev_len);
 
     float* out = p.pool + (static_cast<size_t>(dsl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
 #pragma unroll
@@ -514,7 +744,6 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
     p.src = a->src_slots;
     p.dst = a->dst_slots;
     p.err = a->err_flag;
-    p.kt = reinterpret_cast<uint16_t*>(ws + plan.off_kt);
     p.tp = reinterpret_cast<uint16_t*>(ws + plan.off_tp);
     p.sc = reinterpret_cast<float*>(ws + plan.off_sc);
     p.n_seqs = a->num_seqs;
