@@ -111,6 +111,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
+// 2^x on the hardware exp2 (v_exp_f32). Arguments here are <= 0 decay
+// exponents; results below the normal range flush to zero, which is the
+// decay factor's limit anyway.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // 8 bf16 from two fp32 accumulator quads: slots 0-3 <- a, 4-7 <- b.
 __device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b) {
     u32x4 w;
@@ -304,23 +309,33 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     if (len <= 0 || tend > p.total_tokens || p.dst[n] < 0) return;
     const int j = h / p.group;
 
-    // raw q / k rows in operand layout: xr[tt][ks] = X[16 tt + l16][32 ks + 8 g .. +7]
-    u32x4 kr[4][KS], qr[4][KS];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    // raw k rows in operand layout: kr[tt][ks] = K[16 tt + l16][32 ks + 8 g .. +7]
+    // (q rows are loaded one 16-row tile at a time below, to keep the
+    // register footprint, and with it the wave count per SIMD, in check)
+    const auto load_rows = [&](const uint16_t* x, int tt, u32x4* dst) {
         const int r = 16 * tt + l16;
         const size_t base = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + 8 * g4;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (r < len) {
-                kr[tt][ks] = *reinterpret_cast<const u32x4*>(p.k + base + 32 * ks);
-                qr[tt][ks] = *reinterpret_cast<const u32x4*>(p.q + base + 32 * ks);
-            } else {
-                kr[tt][ks] = u32x4{0u, 0u, 0u, 0u};
-                qr[tt][ks] = u32x4{0u, 0u, 0u, 0u};
+        for (int ks = 0; ks < KS; ++ks)
+            dst[ks] = (r < len) ? *reinterpret_cast<const u32x4*>(x + base + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+    };
+    // sum of squares of the row held in operand layout, over all four lane groups
+    const auto row_sumsq = [&](const u32x4* xr) {
+        float acc = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = __uint_as_float(xr[ks][e] << 16), x1 = __uint_as_float(xr[ks][e] & 0xffff0000u);
+                acc += x0 * x0 + x1 * x1;
             }
-        }
-    }
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        return acc;
+    };
+    u32x4 kr[4][KS];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) load_rows(p.k, tt, kr[tt]);
     // per-token g, beta; cumulative log-decay by an inclusive lane scan
     float gl = 0.f, bl = 0.f;
     if (lane < len) {
@@ -328,7 +343,8 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         gl = p.g[gi];
         bl = p.beta[gi];
     }
-    float gam = gl;
+    // in base 2 (gamma log2(e)), so every decay factor is one hardware exp2
+    float gam = gl * 1.4426950408889634f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const float t = __shfl_up(gam, off);
@@ -337,48 +353,28 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     const float gam_last = __shfl(gam, 63);   // padded tokens add g = 0
     sGam[lane] = gam;
     sBeta[lane] = bl;
-
-    // L2 norms of rows 16 tt + l16 (fp32 sums of exact bf16 squares)
+    // L2 norms of the k rows (fp32 sums of exact bf16 squares)
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float k0 = __uint_as_float(kr[tt][ks][e] << 16), k1 = __uint_as_float(kr[tt][ks][e] & 0xffff0000u);
-                const float q0 = __uint_as_float(qr[tt][ks][e] << 16), q1 = __uint_as_float(qr[tt][ks][e] & 0xffff0000u);
-                sk += k0 * k0 + k1 * k1;
-                sq += q0 * q0 + q1 * q1;
-            }
-        }
-        sk += __shfl_xor(sk, 16);
-        sq += __shfl_xor(sq, 16);
-        sk += __shfl_xor(sk, 32);
-        sq += __shfl_xor(sq, 32);
+        const float sk = row_sumsq(kr[tt]);
         const int r = 16 * tt + l16;
-        if (g4 == 0) {
-            const bool live = r < len;
-            sRk[r] = live ? 1.0f / sqrtf(sk + p.eps) : 0.f;
-            sRq[r] = live ? p.scale / sqrtf(sq + p.eps) : 0.f;
-        }
+        if (g4 == 0) sRk[r] = (r < len) ? 1.0f / sqrtf(sk + p.eps) : 0.f;
     }
     lds_barrier();
-    {
-        const float rk = sRk[lane], rq = sRq[lane];
-        const float eg = expf(gam);
-        float* scp = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScRows * kC);
-        scp[kScX * kC + lane] = eg * rk;
-        scp[kScBeta * kC + lane] = bl;
-        scp[kScZ * kC + lane] = eg * rq;
-        scp[kScD * kC + lane] = rk * expf(gam_last - gam);
-        scp[kScE * kC + lane] = expf(gam_last);
-    }
 
-    // Gram tiles on MFMA: A (strictly lower) -> LDS transposed, P -> workspace.
+    // Gram tiles on MFMA, one row tile at a time: A (strictly lower) -> LDS
+    // transposed, P -> workspace. The q rows of tile tr also give their norms.
     uint16_t* Pg = p.tp + ((static_cast<size_t>(c) * p.hv + h) * 2 + 1) * (kC * kC);
 #pragma unroll
     for (int tr = 0; tr < 4; ++tr) {
+        u32x4 qr[KS];
+        load_rows(p.q, tr, qr);
+        {
+            const float sq = row_sumsq(qr);
+            const int r = 16 * tr + l16;
+            if (g4 == 0) sRq[r] = (r < len) ? p.scale / sqrtf(sq + p.eps) : 0.f;
+        }
+        lds_barrier();
 #pragma unroll
         for (int ts = 0; ts < 4; ++ts) {
             if (ts > tr) {
@@ -391,7 +387,7 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
             for (int ks = 0; ks < KS; ++ks) {
                 const bf16x8 bk = as_bf16x8(kr[ts][ks]);
                 kk = mfma16(as_bf16x8(kr[tr][ks]), bk, kk);
-                qk = mfma16(as_bf16x8(qr[tr][ks]), bk, qk);
+                qk = mfma16(as_bf16x8(qr[ks]), bk, qk);
             }
             const int s = 16 * ts + l16;
             const float gs = sGam[s], rks = sRk[s];
@@ -399,7 +395,7 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * tr + 4 * g4 + i;
-                const float dec = (s <= r) ? expf(sGam[r] - gs) : 0.f;
+                const float dec = (s <= r) ? exp2_hw(sGam[r] - gs) : 0.f;
                 a[i] = (s < r) ? sBeta[r] * dec * kk[i] * sRk[r] * rks : 0.f;
                 Pg[r * kC + s] = f32_to_bf16(dec * qk[i] * sRq[r] * rks);
             }
@@ -407,12 +403,23 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         }
     }
     lds_barrier();
+    {
+        const float rk = sRk[lane], rq = sRq[lane];
+        const float eg = exp2_hw(gam);
+        float* scp = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScRows * kC);
+        scp[kScX * kC + lane] = eg * rk;
+        scp[kScBeta * kC + lane] = bl;
+        scp[kScZ * kC + lane] = eg * rq;
+        scp[kScD * kC + lane] = rk * exp2_hw(gam_last - gam);
+        scp[kScE * kC + lane] = exp2_hw(gam_last);
+    }
 
     // T = (I + A)^-1, right-looking: lane t owns column t of T. Step s fixes
     // x_s and adds A[r][s] x_s to every later row r; only x_s's own update is
-    // on the serial chain. The address of column s of A is tied to x_{s-2}
-    // through an empty asm so at most two columns are in flight (otherwise
-    // the scheduler hoists every load and spills).
+    // on the serial chain. The address of column s of A is tied to x_{s-1}
+    // through an empty asm so one column is in flight at a time (otherwise
+    // the scheduler hoists every load and spills); the other waves on the
+    // SIMD cover the LDS latency.
     float x[kC];
 #pragma unroll
     for (int r = 0; r < kC; ++r) x[r] = 0.f;
@@ -421,7 +428,7 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         x[s] = ((s == lane) ? 1.f : 0.f) - x[s];
         if (s == kC - 1) break;
         int col_off = s * SA;
-        if (s >= 2) __asm__ volatile("" : "+v"(col_off) : "v"(x[s - 2]));
+        __asm__ volatile("" : "+v"(col_off) : "v"(x[s]));
         const float* acol = sAt + col_off;
         const float xs = x[s];
 #pragma unroll
