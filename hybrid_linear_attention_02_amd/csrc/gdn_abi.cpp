@@ -6,6 +6,7 @@
 // device-to-host round trip); gdn_state_pool_validate checks a host copy, and
 // the kernels skip and flag out-of-range indices.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -82,7 +83,7 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
         return fail(GDN_E_INVALID, "gdn_prefill_chunked: scale must be finite and l2_eps finite and >= 0");
     const int32_t n = a->num_seqs;
     if (n > 65535) return fail(GDN_E_INVALID, "gdn_prefill_chunked: at most 65535 sequences per call");
-    int64_t chunks = 0;
+    int64_t chunks = 0, max_chunks = 0;
     if (n > 0) {
         if (a->cu_seqlens_host == nullptr || a->cu_seqlens == nullptr)
             return fail(GDN_E_INVALID, "gdn_prefill_chunked: cu_seqlens (device and host mirror) required");
@@ -91,6 +92,7 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
             const int64_t len = static_cast<int64_t>(a->cu_seqlens_host[i + 1]) - a->cu_seqlens_host[i];
             if (len < 0) return fail(GDN_E_INVALID, "gdn_prefill_chunked: cu_seqlens must be non-decreasing");
             chunks += (len + 63) / 64;
+            max_chunks = std::max<int64_t>(max_chunks, (len + 63) / 64);
         }
         if (a->cu_seqlens_host[n] != a->total_tokens)
             return fail(GDN_E_INVALID, "gdn_prefill_chunked: cu_seqlens[N] != total_tokens");
@@ -100,14 +102,39 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     if (chunks * a->num_v_heads > INT32_MAX / 2)
         return fail(GDN_E_INVALID, "gdn_prefill_chunked: too many chunks");
     plan->num_chunks = static_cast<int32_t>(chunks);
+    // Split long sequences when the longest chunk chain is more than twice the
+    // average per-CU load of one pass (the recurrence runs one workgroup per
+    // (sequence, value head, 64 value columns)).
+    const int64_t wgs_per_seq = static_cast<int64_t>(a->num_v_heads) * ((a->dv + 63) / 64);
+    const int64_t avg_load = (chunks * wgs_per_seq + kNumCUs - 1) / kNumCUs;
+    // (the transition columns and the chain pass work in 64-column groups)
+    const bool can_split = a->dk >= 64 && a->dv >= 64;
+    plan->seg_len = (can_split && max_chunks > kSegChunks && max_chunks > 2 * avg_load) ? kSegChunks : 0;
+    int64_t segs = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const int64_t c = (static_cast<int64_t>(a->cu_seqlens_host[i + 1]) - a->cu_seqlens_host[i] + 63) / 64;
+        segs += (plan->seg_len == 0 || c <= plan->seg_len) ? 1 : (c + plan->seg_len - 1) / plan->seg_len;
+    }
+    if (segs > 65535) return fail(GDN_E_INVALID, "gdn_prefill_chunked: too many sequence segments");
+    plan->num_segs = static_cast<int32_t>(segs);
+    const bool split = plan->seg_len > 0;
+    const size_t hv = static_cast<size_t>(a->num_v_heads), dk = static_cast<size_t>(a->dk), dv = static_cast<size_t>(a->dv);
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     size_t off = 0;
     plan->off_chunk_offsets = off;
     off = up(off + sizeof(int32_t) * static_cast<size_t>(n + 1));
+    plan->off_seg_offsets = off;
+    off = up(off + sizeof(int32_t) * static_cast<size_t>(n + 1));
     plan->off_tp = off;
-    off = up(off + 2ull * chunks * a->num_v_heads * 2 * 64 * 64);
+    off = up(off + 2ull * chunks * hv * 2 * 64 * 64);
     plan->off_sc = off;
-    off = up(off + 4ull * chunks * a->num_v_heads * (5 * 64));
+    off = up(off + 4ull * chunks * hv * (5 * 64));
+    plan->off_se = off;
+    off = up(off + (split ? 4ull * segs * hv * dk * dv : 0));
+    plan->off_sm = off;
+    off = up(off + (split ? 2ull * segs * hv * 2 * dk * dk : 0));
+    plan->off_sh = off;
+    off = up(off + (split ? 4ull * segs * hv * dk * dv : 0));
     plan->bytes = off;
     return GDN_OK;
 }

@@ -28,11 +28,27 @@ int fail(int code, const std::string& msg);
 // arguments and return GDN_OK or GDN_E_HIP / GDN_E_UNSUPPORTED.
 int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream);
 
+// Sequence split of long prefills. A sequence of more than seg_len chunks is
+// cut into segments of seg_len chunks; each segment's local end state E and
+// transition M (the dk x dk map the segment applies to its initial state) are
+// computed for all segments at once, chained across segments, and the
+// segments then run their outputs in parallel from their true initial
+// states. It costs about twice the work of one pass, so it is used only when
+// one pass would leave most of the chip idle.
+constexpr int kSegChunks = 16;    // chunks per segment when splitting
+constexpr int kNumCUs = 256;      // MI355X compute units
+
 struct PrefillPlan {
     int32_t num_chunks = 0;       // sum over sequences of ceil(len / 64)
-    size_t off_chunk_offsets = 0; // int32 [N+1]: first chunk index of each sequence
+    int32_t seg_len = 0;          // chunks per segment, 0 = no split (one segment per sequence)
+    int32_t num_segs = 0;         // total segments
+    size_t off_chunk_offsets = 0; // int32 [N+1]: first chunk of each sequence
+    size_t off_seg_offsets = 0;   // int32 [N+1]: first segment of each sequence
     size_t off_tp = 0;            // bf16 [chunks][HV][2][64][64]: T and P
     size_t off_sc = 0;            // float [chunks][HV][5][64]: per-token scale rows
+    size_t off_se = 0;            // float [segs][HV][dk][dv]: local end state E (split only)
+    size_t off_sm = 0;            // bf16 [segs][HV][2][dk][dk]: transition M, high then low part (split only)
+    size_t off_sh = 0;            // float [segs][HV][dk][dv]: segment initial states (split only)
     size_t bytes = 0;
 };
 int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* plan);

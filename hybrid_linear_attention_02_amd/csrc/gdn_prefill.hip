@@ -82,6 +82,13 @@ struct PrefillParams {
     uint16_t* tp;               // [chunks][HV][2][64][64] T then P
     float* sc;                  // [chunks][HV][5][64]    scale rows
     int32_t* chunk_off_w;       // same buffer as chunk_off, written by the prep kernel
+    const int32_t* seg_off;     // [N+1] device (workspace): first segment of each sequence
+    int32_t* seg_off_w;
+    float* se;                  // [segs][HV][DK][DV]   local end state E of each segment (split only)
+    uint16_t* sm;               // [segs][HV][2][DK][DK] transition M, bf16 high and low parts (split only)
+    float* sh;                  // [segs][HV][DK][DV]   initial state of each segment (split only)
+    int32_t seg_len;            // chunks per segment; 0 = one segment per sequence
+    int32_t num_segs;
     int32_t n_seqs;
     int32_t num_chunks;
     int32_t total_tokens;
@@ -261,18 +268,22 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---------------------------------------------------------------------------
-// prep: first chunk index of every sequence
+// prep: first chunk and first segment of every sequence
 // ---------------------------------------------------------------------------
 
 __global__ void chunk_offsets_kernel(PrefillParams p) {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    int32_t acc = 0;
+    int32_t acc = 0, segs = 0;
     for (int i = 0; i < p.n_seqs; ++i) {
         p.chunk_off_w[i] = acc;
+        p.seg_off_w[i] = segs;
         const int32_t len = p.cu[i + 1] - p.cu[i];
-        acc += len > 0 ? (len + kC - 1) / kC : 0;
+        const int32_t nc = len > 0 ? (len + kC - 1) / kC : 0;
+        acc += nc;
+        segs += (p.seg_len == 0 || nc <= p.seg_len) ? 1 : (nc + p.seg_len - 1) / p.seg_len;
     }
     p.chunk_off_w[p.n_seqs] = acc;
+    p.seg_off_w[p.n_seqs] = segs;
 }
 
 // Locate chunk c: the last sequence n with chunk_off[n] <= c.
@@ -469,19 +480,54 @@ struct RecShape {
 // rows x 16 columns per instruction) and read back 16 bytes per lane; a
 // stride of 2 granules more than the width keeps both near conflict-free.
 
-template <int DK, int NW>
+// Work unit of the recurrence: one segment of one sequence (a whole sequence
+// when the prefill is not split).
+struct Segment {
+    int n;          // sequence
+    int c0, c1;     // chunk range [c0, c1)
+    int tb, te;     // token range [tb, te)
+    bool first, last;
+    bool split;     // the sequence has more than one segment
+};
+
+__device__ __forceinline__ Segment locate_segment(const PrefillParams& p, int g) {
+    Segment sg;
+    sg.n = find_seq(p.seg_off, p.n_seqs, g);
+    const int k = g - p.seg_off[sg.n];
+    const int nseg = p.seg_off[sg.n + 1] - p.seg_off[sg.n];
+    const int cs = p.chunk_off[sg.n], ce = p.chunk_off[sg.n + 1];
+    sg.first = k == 0;
+    sg.last = k == nseg - 1;
+    sg.split = nseg > 1;
+    sg.c0 = nseg == 1 ? cs : cs + k * p.seg_len;
+    sg.c1 = sg.last ? ce : sg.c0 + p.seg_len;
+    sg.tb = p.cu[sg.n] + (sg.c0 - cs) * kC;
+    sg.te = sg.last ? p.cu[sg.n + 1] : sg.tb + (sg.c1 - sg.c0) * kC;
+    return sg;
+}
+
+// Modes of the recurrence kernel.
+enum : int {
+    kModeOutput = 0,   // outputs o, state from the slot / zero / segment initial state, final state to the slot
+    kModeState = 1,    // split pass 1: no outputs; columns [0, dv) carry the state from zero with V,
+                       // columns [dv, dv + dk) carry the identity with V = 0 (the transition M);
+                       // results to the segment buffers
+};
+
+template <int DK, int NW, int MODE>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 prefill_recurrent_kernel(PrefillParams p) {
     using S = RecShape<DK, NW>;
     constexpr int NT = S::NT, NV = S::NV, KS = S::KS, MT = S::MT;
     constexpr int SV = S::SV, SO = S::SO;
     constexpr int KQ = S::KQ, TP = S::TP, VV = S::VV, SCN = S::SCN;
+    constexpr bool OUT = MODE == kModeOutput;
     __shared__ __align__(16) uint16_t sK[kC * DK];   // swizzled, see kq_swz
-    __shared__ __align__(16) uint16_t sQ[kC * DK];
+    __shared__ __align__(16) uint16_t sQ[OUT ? kC * DK : 8];
     __shared__ __align__(16) uint16_t sT[kC * kC];   // swizzled, see tp_off
-    __shared__ __align__(16) uint16_t sP[kC * kC];
+    __shared__ __align__(16) uint16_t sP[OUT ? kC * kC : 8];
     __shared__ __align__(16) uint16_t sV[kC * SV];
-    __shared__ __align__(16) uint16_t sO[kC * SO];
+    __shared__ __align__(16) uint16_t sO[OUT ? kC * SO : 8];
     __shared__ __align__(16) float sSc[kScRows * kC];
 
     const int tid = threadIdx.x;
@@ -495,31 +541,46 @@ prefill_recurrent_kernel(PrefillParams p) {
     const int hig = rest % p.group;
     const int grp = rest / p.group;
     const int h = j * p.group + hig;
-    const int n = blockIdx.y;
+    const Segment sg = locate_segment(p, blockIdx.y);
+    const int n = sg.n;
+    if (!OUT && sg.last) return;              // the last segment's end state is not needed
 
     const int dsl = p.dst[n];
     if (dsl < 0) return;
     const int ssl = p.src[n];
-    const int tb = p.cu[n], te = p.cu[n + 1];
-    const int c0 = p.chunk_off[n], c1 = p.chunk_off[n + 1];
+    const int tb = sg.tb, te = sg.te;
+    const int c0 = sg.c0, c1 = sg.c1;
     if (dsl >= p.num_slots || ssl >= p.num_slots || te > p.total_tokens || te < tb || c1 > p.num_chunks) {
         if (tid == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
         return;
     }
-    const int vcol0 = grp * NV;                 // first value column of the workgroup
-    const int col = vcol0 + wave * 16 + l16;    // this lane's value column
+    // columns of this workgroup: value columns [vcol0, vcol0 + NV); in the
+    // state pass, groups past dv carry columns of the transition instead
+    const int ncg = p.dv / NV;
+    const bool m_cols = !OUT && grp >= ncg;
+    const int vcol0 = (m_cols ? grp - ncg : grp) * NV;
+    const int col = vcol0 + wave * 16 + l16;    // this lane's column (value or transition)
 
     // fp32 master state: H[mu][i] = H[16 mu + 4 g + i][col]
     f32x4 H[MT];
-    if (ssl >= 0) {
-        const float* st = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+    const float* init = nullptr;
+    if (OUT) {
+        // A split sequence starts every segment, the first included, from the
+        // chained initial states: the source slot is then read only by pass 2,
+        // before the last segment may overwrite it in place.
+        if (sg.split) init = p.sh + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+        else if (ssl >= 0) init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+    }
+    if (init != nullptr) {
 #pragma unroll
         for (int mu = 0; mu < MT; ++mu)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) H[mu][i] = st[(16 * mu + 4 * g4 + i) * p.dv + col];
+            for (int i = 0; i < 4; ++i) H[mu][i] = init[(16 * mu + 4 * g4 + i) * p.dv + col];
     } else {
 #pragma unroll
-        for (int mu = 0; mu < MT; ++mu) H[mu] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) H[mu][i] = (m_cols && 16 * mu + 4 * g4 + i == col) ? 1.f : 0.f;
     }
 
     // register staging of one chunk's operands (the next chunk is fetched
@@ -532,13 +593,12 @@ prefill_recurrent_kernel(PrefillParams p) {
         for (int m = 0; m < KQ; ++m) {
             const int idx = tid + NT * m;
             const int r = idx / (DK / 8), c8 = idx % (DK / 8);
+            rK[m] = u32x4{0u, 0u, 0u, 0u};
+            rQ[m] = u32x4{0u, 0u, 0u, 0u};
             if (r < len) {
                 const size_t off = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + c8 * 8;
                 rK[m] = *reinterpret_cast<const u32x4*>(p.k + off);
-                rQ[m] = *reinterpret_cast<const u32x4*>(p.q + off);
-            } else {
-                rK[m] = u32x4{0u, 0u, 0u, 0u};
-                rQ[m] = u32x4{0u, 0u, 0u, 0u};
+                if (OUT) rQ[m] = *reinterpret_cast<const u32x4*>(p.q + off);
             }
         }
         const uint16_t* TPg = p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC);
@@ -546,14 +606,14 @@ prefill_recurrent_kernel(PrefillParams p) {
         for (int m = 0; m < TP; ++m) {
             const int idx = tid + NT * m;
             rT[m] = *reinterpret_cast<const u32x4*>(TPg + 8 * idx);
-            rP[m] = *reinterpret_cast<const u32x4*>(TPg + kC * kC + 8 * idx);
+            if (OUT) rP[m] = *reinterpret_cast<const u32x4*>(TPg + kC * kC + 8 * idx);
         }
 #pragma unroll
         for (int m = 0; m < VV; ++m) {
             const int idx = tid + NT * m;
             const int r = idx / (NV / 8), c8 = idx % (NV / 8);
             rV[m] = u32x4{0u, 0u, 0u, 0u};
-            if (r < len)
+            if (r < len && !m_cols)
                 rV[m] = *reinterpret_cast<const u32x4*>(p.v + (static_cast<size_t>(t0 + r) * p.hv + h) * p.dv + vcol0 + 8 * c8);
         }
         const float* SCg = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScRows * kC);
@@ -569,14 +629,14 @@ prefill_recurrent_kernel(PrefillParams p) {
             const int idx = tid + NT * m;
             const int r = idx / (DK / 8), c8 = idx % (DK / 8);
             *reinterpret_cast<u32x4*>(sK + kq_off<DK, false>(r, c8 * 8)) = rK[m];
-            *reinterpret_cast<u32x4*>(sQ + kq_off<DK, true>(r, c8 * 8)) = rQ[m];
+            if (OUT) *reinterpret_cast<u32x4*>(sQ + kq_off<DK, true>(r, c8 * 8)) = rQ[m];
         }
 #pragma unroll
         for (int m = 0; m < TP; ++m) {
             const int idx = tid + NT * m;
             const int r = idx / 8, c8 = idx % 8;
             *reinterpret_cast<u32x4*>(sT + tp_off<false>(r, c8 * 8)) = rT[m];
-            *reinterpret_cast<u32x4*>(sP + tp_off<true>(r, c8 * 8)) = rP[m];
+            if (OUT) *reinterpret_cast<u32x4*>(sP + tp_off<true>(r, c8 * 8)) = rP[m];
         }
 #pragma unroll
         for (int m = 0; m < VV; ++m) {
@@ -607,19 +667,18 @@ prefill_recurrent_kernel(PrefillParams p) {
     for (int c = c0; c < c1; ++c) {
         const int t0 = tb + (c - c0) * kC;
         const int len = min(kC, te - t0);
-        lds_barrier();                 // previous chunk's LDS reads and sO writes are done
-        if (prev_len > 0) store_o(prev_t0, prev_len);
+        lds_barrier();                   // previous chunk's LDS reads and sO writes are done
+        if (OUT && prev_len > 0) store_o(prev_t0, prev_len);
         stage();
         lds_barrier();
         if (c + 1 < c1) fetch(c + 1);    // in flight while this chunk is computed
 
-        // X = K H and Z = Q H  (contraction over dk)
+        // X = K H and Z = Q H  (contraction over dk). k-step outer, row tile
+        // inner: each step reads its operands first and then issues its
+        // independent MFMAs, so LDS latency overlaps the matrix pipe.
         bf16x8 hb[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) hb[ks] = pack8(H[2 * ks], H[2 * ks + 1]);
-        // k-step outer, row tile inner: each step reads its 8 operands first and
-        // then issues 8 independent MFMAs, so LDS latency overlaps the matrix
-        // pipe instead of stalling every instruction.
         f32x4 X[4], Z[4];
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
@@ -632,12 +691,12 @@ prefill_recurrent_kernel(PrefillParams p) {
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
                 ak[tau] = kq_pair<DK, false>(sK, 16 * tau + l16, 32 * ks, g4);
-                aq[tau] = kq_pair<DK, true>(sQ, 16 * tau + l16, 32 * ks, g4);
+                if (OUT) aq[tau] = kq_pair<DK, true>(sQ, 16 * tau + l16, 32 * ks, g4);
             }
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
                 X[tau] = mfma16(ak[tau], hb[ks], X[tau]);
-                Z[tau] = mfma16(aq[tau], hb[ks], Z[tau]);
+                if (OUT) Z[tau] = mfma16(aq[tau], hb[ks], Z[tau]);
             }
         }
         // Y = diag(beta) (V - diag(exp(gamma) rk) X)
@@ -658,17 +717,19 @@ prefill_recurrent_kernel(PrefillParams p) {
             U[tau] = mfma16(tp_pair<false>(sT, 16 * tau + l16, 0, g4), yb0, f32x4{0.f, 0.f, 0.f, 0.f});
             if (tau >= 2) U[tau] = mfma16(tp_pair<false>(sT, 16 * tau + l16, 32, g4), yb1, U[tau]);
         }
-        const bf16x8 ub0 = pack8(U[0], U[1]), ub1 = pack8(U[2], U[3]);
-        // O = diag(exp(gamma) rq) Z + P U  -> staged in LDS as bf16
+        if (OUT) {
+            // O = diag(exp(gamma) rq) Z + P U  -> staged in LDS as bf16
+            const bf16x8 ub0 = pack8(U[0], U[1]), ub1 = pack8(U[2], U[3]);
 #pragma unroll
-        for (int tau = 0; tau < 4; ++tau) {
-            f32x4 O = mfma16(tp_pair<true>(sP, 16 * tau + l16, 0, g4), ub0, f32x4{0.f, 0.f, 0.f, 0.f});
-            if (tau >= 2) O = mfma16(tp_pair<true>(sP, 16 * tau + l16, 32, g4), ub1, O);
-            const int r0 = 16 * tau + 4 * g4;
-            const f32x4 sz = *reinterpret_cast<const f32x4*>(sSc + kScZ * kC + r0);
-            O += sz * Z[tau];
+            for (int tau = 0; tau < 4; ++tau) {
+                f32x4 O = mfma16(tp_pair<true>(sP, 16 * tau + l16, 0, g4), ub0, f32x4{0.f, 0.f, 0.f, 0.f});
+                if (tau >= 2) O = mfma16(tp_pair<true>(sP, 16 * tau + l16, 32, g4), ub1, O);
+                const int r0 = 16 * tau + 4 * g4;
+                const f32x4 sz = *reinterpret_cast<const f32x4*>(sSc + kScZ * kC + r0);
+                O += sz * Z[tau];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sO[(r0 + i) * SO + wave * 16 + l16] = f32_to_bf16(O[i]);
+                for (int i = 0; i < 4; ++i) sO[(r0 + i) * SO + wave * 16 + l16] = f32_to_bf16(O[i]);
+            }
         }
         // H' = exp(gamma_last) H + K^T diag(rk exp(gamma_last - gamma)) U
         f32x4 DU[4];
@@ -696,14 +757,134 @@ prefill_recurrent_kernel(PrefillParams p) {
         prev_t0 = t0;
         prev_len = len;
     }
-    lds_barrier();
-    if (prev_len > 0) store_o(prev_t0, prev_len);
+    if (OUT) {
+        lds_barrier();
+        if (prev_len > 0) store_o(prev_t0, prev_len);
+        if (!sg.last) return;               // a middle segment's end state is the next one's start (pass 2)
+        float* out = p.pool + (static_cast<size_t>(dsl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[(16 * mu + 4 * g4 + i) * p.dv + col] = H[mu][i];
+    } else if (!m_cols) {
+        float* out = p.se + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[(16 * mu + 4 * g4 + i) * p.dv + col] = H[mu][i];
+    } else {
+        // transition M[d][m] (m = col), as bf16 high part and the bf16 rounding of the remainder
+        uint16_t* out = p.sm + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (2 * DK * DK);
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = H[mu][i];
+                const uint16_t hi = f32_to_bf16(x);
+                const size_t e_off = static_cast<size_t>(16 * mu + 4 * g4 + i) * DK + col;
+                out[e_off] = hi;
+                out[DK * DK + e_off] = f32_to_bf16(x - bf16_to_f32(hi));
+            }
+    }
+}
 
-    float* out = p.pool + (static_cast<size_t>(dsl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+// ---------------------------------------------------------------------------
+// split pass 2: chain the segments of each split sequence,
+// H_{s+1} = M_s H_s + E_s, one workgroup per (sequence, value head, 64 value
+// columns), one wave per 16 columns. Writes every segment's initial state
+// (the first one copied from the source slot or zero). The products are bf16
+// MFMAs on high/low splits of both factors (M_hi H_hi + M_hi H_lo + M_lo H_hi),
+// which keeps about 16 bits of the fp32 state.
+// ---------------------------------------------------------------------------
+
+template <int DK>
+__global__ void __launch_bounds__(256) segment_chain_kernel(PrefillParams p) {
+    constexpr int MT = DK / 16, KS = DK / 32;
+    constexpr int NT = 256;
+    constexpr int MPT = 2 * DK * DK / 8 / NT;   // 16-byte pieces of M (high and low) per thread
+    // M_s, high and low parts, staged whole in LDS per segment (swizzled like
+    // the k tiles: conflict-free row-operand reads)
+    __shared__ __align__(16) uint16_t sMh[DK * DK];
+    __shared__ __align__(16) uint16_t sMl[DK * DK];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int groups = p.dv / 64;
+    const int h = blockIdx.x / groups;
+    const int col = (blockIdx.x - h * groups) * 64 + wave * 16 + l16;
+    const int n = blockIdx.y;
+    const int g0 = p.seg_off[n], g1 = p.seg_off[n + 1];
+    if (g1 - g0 < 2) return;                    // not split
+    const int dsl = p.dst[n], ssl = p.src[n];
+    if (dsl < 0 || dsl >= p.num_slots || ssl >= p.num_slots) return;   // skipped or flagged by pass 3
+
+    const size_t tile = static_cast<size_t>(DK) * p.dv;
+    f32x4 H[MT];
+    if (ssl >= 0) {
+        const float* st = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * tile;
 #pragma unroll
-    for (int mu = 0; mu < MT; ++mu)
+        for (int mu = 0; mu < MT; ++mu)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[(16 * mu + 4 * g4 + i) * p.dv + col] = H[mu][i];
+            for (int i = 0; i < 4; ++i) H[mu][i] = st[(16 * mu + 4 * g4 + i) * p.dv + col];
+    } else {
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu) H[mu] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int g = g0;; ++g) {
+        float* sh = p.sh + (static_cast<size_t>(g) * p.hv + h) * tile;
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sh[(16 * mu + 4 * g4 + i) * p.dv + col] = H[mu][i];
+        if (g + 1 == g1) break;
+        // issue every load of this segment first: M (all threads), E (own columns)
+        const uint16_t* mg = p.sm + (static_cast<size_t>(g) * p.hv + h) * (2 * DK * DK);
+        u32x4 rm[MPT];
+#pragma unroll
+        for (int m = 0; m < MPT; ++m) rm[m] = *reinterpret_cast<const u32x4*>(mg + 8 * (tid + NT * m));
+        const float* se = p.se + (static_cast<size_t>(g) * p.hv + h) * tile;
+        f32x4 acc[MT];
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mu][i] = se[(16 * mu + 4 * g4 + i) * p.dv + col];
+        // B operands: high and low bf16 parts of H, k = state row
+        bf16x8 bh[KS], bl[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            f32x4 l0, l1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                l0[i] = H[2 * ks][i] - bf16_to_f32(f32_to_bf16(H[2 * ks][i]));
+                l1[i] = H[2 * ks + 1][i] - bf16_to_f32(f32_to_bf16(H[2 * ks + 1][i]));
+            }
+            bh[ks] = pack8(H[2 * ks], H[2 * ks + 1]);
+            bl[ks] = pack8(l0, l1);
+        }
+        lds_barrier();                          // previous segment's LDS reads are done
+#pragma unroll
+        for (int m = 0; m < MPT; ++m) {
+            const int e0 = 8 * (tid + NT * m);   // element of [2][DK][DK]
+            const int part = e0 / (DK * DK), rem = e0 - part * DK * DK;
+            const int r = rem / DK, c = rem - r * DK;
+            *reinterpret_cast<u32x4*>((part ? sMl : sMh) + kq_off<DK, false>(r, c)) = rm[m];
+        }
+        lds_barrier();
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu) {
+            const int row = 16 * mu + l16;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 ah = kq_pair<DK, false>(sMh, row, 32 * ks, g4);
+                const bf16x8 al = kq_pair<DK, false>(sMl, row, 32 * ks, g4);
+                acc[mu] = mfma16(ah, bh[ks], acc[mu]);
+                acc[mu] = mfma16(ah, bl[ks], acc[mu]);
+                acc[mu] = mfma16(al, bh[ks], acc[mu]);
+            }
+        }
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu) H[mu] = acc[mu];
+    }
 }
 
 int check_launch(const char* what) {
@@ -713,19 +894,36 @@ int check_launch(const char* what) {
     return GDN_OK;
 }
 
+template <int DK, int MODE>
+void launch_recurrence(const PrefillParams& p, int nw, int groups, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(p.hv * groups), static_cast<unsigned>(p.num_segs));
+    switch (nw) {
+        case 1: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 1, MODE>), grid, dim3(64), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 2, MODE>), grid, dim3(128), 0, s, p); break;
+        default: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 4, MODE>), grid, dim3(256), 0, s, p); break;
+    }
+}
+
 template <int DK>
-int launch_dk(const PrefillParams& p, int n_seqs, int nw, hipStream_t s) {
+int launch_dk(const PrefillParams& p, int nw, hipStream_t s) {
     if (p.num_chunks > 0) {
         hipLaunchKernelGGL((prefill_intra_kernel<DK>), dim3(p.num_chunks, p.hv), dim3(64), 0, s, p);
         const int st = check_launch("intra-chunk");
         if (st != GDN_OK) return st;
     }
-    const dim3 grid(static_cast<unsigned>(p.hv * (p.dv / (16 * nw))), static_cast<unsigned>(n_seqs));
-    switch (nw) {
-        case 1: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 1>), grid, dim3(64), 0, s, p); break;
-        case 2: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 2>), grid, dim3(128), 0, s, p); break;
-        default: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 4>), grid, dim3(256), 0, s, p); break;
+    const int groups = p.dv / (16 * nw);
+    if (p.seg_len > 0) {
+        // pass 1: every segment's local end state (value columns) and
+        // transition (dk identity columns), all segments at once
+        launch_recurrence<DK, kModeState>(p, nw, groups + DK / (16 * nw), s);
+        int st = check_launch("segment state pass");
+        if (st != GDN_OK) return st;
+        // pass 2: chain the segments
+        hipLaunchKernelGGL((segment_chain_kernel<DK>), dim3(p.hv * (p.dv / 64), p.n_seqs), dim3(256), 0, s, p);
+        st = check_launch("segment chain");
+        if (st != GDN_OK) return st;
     }
+    launch_recurrence<DK, kModeOutput>(p, nw, groups, s);
     return check_launch("recurrence");
 }
 
@@ -753,6 +951,13 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
     p.err = a->err_flag;
     p.tp = reinterpret_cast<uint16_t*>(ws + plan.off_tp);
     p.sc = reinterpret_cast<float*>(ws + plan.off_sc);
+    p.seg_off = reinterpret_cast<const int32_t*>(ws + plan.off_seg_offsets);
+    p.seg_off_w = reinterpret_cast<int32_t*>(ws + plan.off_seg_offsets);
+    p.se = reinterpret_cast<float*>(ws + plan.off_se);
+    p.sm = reinterpret_cast<uint16_t*>(ws + plan.off_sm);
+    p.sh = reinterpret_cast<float*>(ws + plan.off_sh);
+    p.seg_len = plan.seg_len;
+    p.num_segs = plan.num_segs;
     p.n_seqs = a->num_seqs;
     p.num_chunks = plan.num_chunks;
     p.total_tokens = a->total_tokens;
@@ -769,9 +974,9 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
     if (st != GDN_OK) return st;
     const int nw = a->dv >= 64 ? 4 : a->dv / 16;
     switch (a->dk) {
-        case 32: return launch_dk<32>(p, a->num_seqs, nw, s);
-        case 64: return launch_dk<64>(p, a->num_seqs, nw, s);
-        case 128: return launch_dk<128>(p, a->num_seqs, nw, s);
+        case 32: return launch_dk<32>(p, nw, s);
+        case 64: return launch_dk<64>(p, nw, s);
+        case 128: return launch_dk<128>(p, nw, s);
         default: return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: unsupported dk");
     }
 }

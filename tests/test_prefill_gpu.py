@@ -260,3 +260,49 @@ def test_long_packed_prefill_sampled():
                                       as_f64(tk.v[a:b, :2], BF16), tk.g[a:b, :2], tk.beta[a:b, :2], 128 ** -0.5, EPS)
     check_outputs(og[a:b, heads], o_ref, BF16, f"seq {n}")
     check_state(st[n].cpu().numpy()[heads], h_ref, BF16, f"seq {n} state")
+
+
+# --- long sequences cut into segments (pass 1: segment end states and
+# transitions, pass 2: chained initial states, pass 3: outputs per segment) ---
+
+def test_split_long_and_short_sequences_from_slots():
+    """A 3000-token sequence (47 chunks, split into 3 segments of up to 16
+    chunks because one pass would leave the chip idle) packed with a
+    100-token one; both resume from pool states."""
+    lengths = [3000, 100]
+    src = [0, 1]
+    dst = [2, 3]
+    pw = prefill_workload("split_long_short", seed=61, lengths=lengths, HK=2, HV=4, dk=128, dv=128, dtype=BF16,
+                          num_slots=4, pool_sigma=0.05, src=src)
+    o, st, _ = _gpu_prefill(pw, src, dst)
+    _check(pw, o, st, src, dst)
+    np.testing.assert_array_equal(st.cpu().numpy()[:2], pw.pool[:2])
+
+
+@pytest.mark.parametrize("variant", ["low_decay", "no_decay_small_beta"])
+def test_split_in_place_weak_decay(variant):
+    """In place (src == dst) on a split 2500-token sequence with weak decay,
+    so the chained segment states carry real information into every output;
+    the source slot is read before the last segment overwrites it."""
+    kw = {"low_decay": dict(g_range=(1e-4, 1e-2)),
+          "no_decay_small_beta": dict(g_range=(0.0, 0.0), beta_mode=0.05)}[variant]
+    lengths = [2500]
+    src = [1]
+    dst = [1]
+    pw = prefill_workload("split_inplace_" + variant, seed=67, lengths=lengths, HK=1, HV=2, dk=128, dv=128,
+                          dtype=BF16, num_slots=2, pool_sigma=0.05, src=src, **kw)
+    o, st, _ = _gpu_prefill(pw, src, dst)
+    _check(pw, o, st, src, dst)
+    np.testing.assert_array_equal(st.cpu().numpy()[0], pw.pool[0])
+
+
+def test_split_dk_ne_dv():
+    """Split path with dk = 64, dv = 128 (transition columns dk, value
+    columns dv) and a zero initial state."""
+    lengths = [1700, 64]
+    src = [-1, 0]
+    dst = [1, 2]
+    pw = prefill_workload("split_64x128", seed=71, lengths=lengths, HK=2, HV=4, dk=64, dv=128, dtype=BF16,
+                          num_slots=3, pool_sigma=0.05, src=src, g_range=(1e-3, 5e-2))
+    o, st, _ = _gpu_prefill(pw, src, dst)
+    _check(pw, o, st, src, dst)
