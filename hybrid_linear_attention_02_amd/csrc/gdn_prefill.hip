@@ -39,6 +39,7 @@
 // decay factors are applied as fp32 row scales on the accumulator side.
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include <cstdint>
 #include <string>
@@ -79,7 +80,8 @@ struct PrefillParams {
     const int32_t* src;
     const int32_t* dst;
     int32_t* err;
-    uint16_t* tp;               // [chunks][HV][2][64][64] T then P
+    uint16_t* tp;               // [chunks][HV][2][64 * 64] T (row-major), then P as row-operand fragments
+    uint16_t* qf;               // [chunks][HK][64 * DK] q rows as row-operand fragments
     float* sc;                  // [chunks][HV][5][64]    scale rows
     int32_t* chunk_off_w;       // same buffer as chunk_off, written by the prep kernel
     const int32_t* seg_off;     // [N+1] device (workspace): first segment of each sequence
@@ -100,6 +102,39 @@ struct PrefillParams {
     float scale;
     float eps;
 };
+
+// Uniform base pointer plus a 32-bit per-lane byte offset: lets the compiler
+// use the scalar-base global access form (no 64-bit address per lane).
+template <typename T, typename B>
+__device__ __forceinline__ T* at_bytes(B* base, unsigned byte_off) {
+    using C = typename std::conditional<std::is_const<B>::value, const char, char>::type;
+    return reinterpret_cast<T*>(reinterpret_cast<C*>(base) + byte_off);
+}
+template <typename T, typename B>
+__device__ __forceinline__ const T* at_bytes(const B* base, unsigned byte_off) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+// Buffer resources (base, byte range): loads past the range return zero and
+// stores past it are dropped, in hardware, so ragged rows need no branch.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, unsigned off) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, 0, 0);
+}
+// Byte range of `rows` token rows of `width` bf16 values, rows `stride`
+// elements apart (zero rows: an empty range).
+__device__ __forceinline__ unsigned rows_bytes(int rows, unsigned stride, int width) {
+    return rows > 0 ? 2u * ((rows - 1) * stride + width) : 0u;
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
@@ -320,7 +355,9 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     if (len <= 0 || tend > p.total_tokens || p.dst[n] < 0) return;
     const int j = h / p.group;
 
-    // raw k rows in operand layout: kr[tt][ks] = K[16 tt + l16][32 ks + 8 g .. +7]
+    // raw k rows as row operands in natural feature order (a contraction
+    // over dk may order its k slots freely, as long as both operands agree):
+    // kr[tt][ks] = K[16 tt + l16][32 ks + 8 g .. +7]
     // (q rows are loaded one 16-row tile at a time below, to keep the
     // register footprint, and with it the wave count per SIMD, in check)
     const auto load_rows = [&](const uint16_t* x, int tt, u32x4* dst) {
@@ -374,44 +411,65 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     lds_barrier();
 
     // Gram tiles on MFMA, one row tile at a time: A (strictly lower) -> LDS
-    // transposed, P -> workspace. The q rows of tile tr also give their norms.
-    uint16_t* Pg = p.tp + ((static_cast<size_t>(c) * p.hv + h) * 2 + 1) * (kC * kC);
+    // transposed; P -> workspace as row-operand fragments (computed as P^T,
+    // whose accumulator layout puts one P row in each lane). The q rows of
+    // tile tr also give their norms and, once per key head, go to the
+    // workspace as row-operand fragments.
+    u32x4* Pf = reinterpret_cast<u32x4*>(p.tp + ((static_cast<size_t>(c) * p.hv + h) * 2 + 1) * (kC * kC));
+    u32x4* Qf = reinterpret_cast<u32x4*>(p.qf + (static_cast<size_t>(c) * p.hk + j) * (kC * DK));
+    const bool write_q = h % p.group == 0;
 #pragma unroll
     for (int tr = 0; tr < 4; ++tr) {
         u32x4 qr[KS];
         load_rows(p.q, tr, qr);
+        if (write_q) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) Qf[(tr * KS + ks) * 64 + lane] = qr[ks];
+        }
         {
             const float sq = row_sumsq(qr);
             const int r = 16 * tr + l16;
             if (g4 == 0) sRq[r] = (r < len) ? p.scale / sqrtf(sq + p.eps) : 0.f;
         }
         lds_barrier();
+        f32x4 pt[4];                           // pt[ts][i] = P[16 tr + l16][16 ts + 4 g + i]
 #pragma unroll
         for (int ts = 0; ts < 4; ++ts) {
-            if (ts > tr) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Pg[(16 * tr + 4 * g4 + i) * kC + 16 * ts + l16] = 0;
-                continue;
-            }
-            f32x4 kk = f32x4{0.f, 0.f, 0.f, 0.f}, qk = f32x4{0.f, 0.f, 0.f, 0.f};
+            pt[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (ts > tr) continue;
+            f32x4 kk = f32x4{0.f, 0.f, 0.f, 0.f}, kq = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const bf16x8 bk = as_bf16x8(kr[ts][ks]);
                 kk = mfma16(as_bf16x8(kr[tr][ks]), bk, kk);
-                qk = mfma16(as_bf16x8(qr[ks]), bk, qk);
+                kq = mfma16(bk, as_bf16x8(qr[ks]), kq);
             }
-            const int s = 16 * ts + l16;
-            const float gs = sGam[s], rks = sRk[s];
-            f32x4 a;
+            // A[r][s]: row r = 16 tr + 4 g + i, column (lane) s
+            {
+                const int s = 16 * ts + l16;
+                const float gs = sGam[s], rks = sRk[s];
+                f32x4 a;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * tr + 4 * g4 + i;
-                const float dec = (s <= r) ? exp2_hw(sGam[r] - gs) : 0.f;
-                a[i] = (s < r) ? sBeta[r] * dec * kk[i] * sRk[r] * rks : 0.f;
-                Pg[r * kC + s] = f32_to_bf16(dec * qk[i] * sRq[r] * rks);
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * tr + 4 * g4 + i;
+                    const float dec = (s < r) ? exp2_hw(sGam[r] - gs) : 0.f;
+                    a[i] = (s < r) ? sBeta[r] * dec * kk[i] * sRk[r] * rks : 0.f;
+                }
+                *reinterpret_cast<f32x4*>(sAt + s * SA + 16 * tr + 4 * g4) = a;
             }
-            *reinterpret_cast<f32x4*>(sAt + s * SA + 16 * tr + 4 * g4) = a;
+            // P[r][s]: row (lane) r = 16 tr + l16, column s = 16 ts + 4 g + i
+            {
+                const int r = 16 * tr + l16;
+                const float gr = sGam[r], rqr = sRq[r];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = 16 * ts + 4 * g4 + i;
+                    pt[ts][i] = (s <= r) ? exp2_hw(gr - sGam[s]) * kq[i] * rqr * sRk[s] : 0.f;
+                }
+            }
         }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) Pf[(tr * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(pt[2 * ks], pt[2 * ks + 1]));
     }
     lds_barrier();
     {
@@ -456,29 +514,70 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// recurrence: one workgroup per (sequence, value head, 16*NW value columns)
+// recurrence: one workgroup per (segment, value head, NV = 16 NW value columns)
+//
+// Two wave roles, one of each per SIMD:
+//   compute waves (NW, one per 16 value columns) run only the state chain of
+//     each chunk, X = K H, Y, U = T Y, H' = e H + K^T D U, from
+//     double-buffered LDS tiles; in output mode they also publish H (bf16, as
+//     used for X) and U (bf16) of the chunk;
+//   helper waves (4, one per 16-token row block of a chunk) stage the next
+//     chunk's K, T, V and scale rows into the other LDS buffer and, one step
+//     behind, form the outputs O = diag(exp(gamma) rq) Q H + P U of their rows
+//     from q and P rows they load straight into registers and the published
+//     H and U.
+// A step is one chunk for the compute waves; every wave meets one workgroup
+// barrier per step. The state chain, the critical path of a sequence, thus
+// carries no global memory traffic, staging or output work.
 // ---------------------------------------------------------------------------
 
-template <int DK, int NW>
+template <int DK, int NW, int MODE>
 struct RecShape {
-    static constexpr int NT = 64 * NW;        // threads
+    static constexpr bool OUT = MODE == 0;
     static constexpr int NV = 16 * NW;        // value columns per workgroup
+    static constexpr int NA = 64 * NW;        // compute threads (waves 0 .. NW-1)
+    static constexpr int NB = 256;            // helper threads (waves NW .. NW+3)
+    static constexpr int NT = NA + NB;
     static constexpr int KS = DK / 32;        // k-steps over dk
     static constexpr int MT = DK / 16;        // 16-row tiles of the state
-    static constexpr int SV = NV + 16;        // bf16 row strides of the padded tiles (bank note below)
-    static constexpr int SO = NV + 8;
-    static constexpr int KQ = 8 * DK / NT;    // 16-byte pieces per thread: K (and Q) tile
-    static constexpr int TP = 512 / NT;       //                            T (and P) tile
-    static constexpr int VV = 8 * NV / NT;    //                            V tile slice
-    static constexpr int SCN = (kScRows * kC / 4 + NT - 1) / NT;   // scale rows
-    static_assert(KQ * NT == 8 * DK && TP * NT == 512 && VV * NT == 8 * NV, "tile split");
+    static constexpr int SV = NV + 16;        // bf16 row stride of the V slice
+    static constexpr int SO = NV + 8;         // bf16 row stride of a helper's output tile
+    static constexpr int KP = 8 * DK;         // 16-byte pieces: K tile
+    static constexpr int TPP = 512;           //                 T tile
+    static constexpr int VP = 8 * NV;         //                 V slice
+    static constexpr int SCP = kScRows * kC / 4;   //            scale rows
+    static constexpr int KQ = (KP + NB - 1) / NB;  // per helper thread
+    static constexpr int TP = TPP / NB;
+    static constexpr int VV = (VP + NB - 1) / NB;
+    static constexpr int SCN = (SCP + NB - 1) / NB;
+    // LDS layout in bytes; the two buffers of each tile are adjacent so that
+    // one address register serves both (the second through the immediate).
+    static constexpr int SZ_K = kC * DK * 2, SZ_T = kC * kC * 2, SZ_V = kC * SV * 2, SZ_SC = kScRows * kC * 4;
+    static constexpr int SZ_H = NV * DK * 2, SZ_U = NV * kC * 2;
+    static constexpr int L_K = 0;
+    static constexpr int L_T = L_K + 2 * SZ_K;
+    static constexpr int L_V = L_T + 2 * SZ_T;
+    static constexpr int L_SC = L_V + 2 * SZ_V;
+    static constexpr int L_H = L_SC + 2 * SZ_SC;
+    static constexpr int L_U = L_H + (OUT ? 2 * SZ_H : 0);
+    static constexpr int L_O = L_U + (OUT ? 2 * SZ_U : 0);
+    static constexpr int BYTES = L_O + (OUT ? 4 * 16 * SO * 2 : 0);
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(TP * NB == TPP, "tile split");
 };
-// Bank note (same model as for the swizzled tiles): V is read only through
-// the transpose read, 8 rows x 4 granules per pass; a stride of 4 granules
-// more than the tile width (20 granules at 64 columns) spaces those rows 4 or
-// more granules apart. The output staging tile is written 2 bytes per lane (4
-// rows x 16 columns per instruction) and read back 16 bytes per lane; a
-// stride of 2 granules more than the width keeps both near conflict-free.
+
+// Column-major bf16 tiles exchanged between the two roles (H: NV columns of
+// DK features in natural order, 16-byte piece j = features 8 j .. 8 j + 7;
+// U: NV columns of 64 tokens, piece j = tokens 32 (j / 4) + {4 (j % 4) + e,
+// 16 + 4 (j % 4) + e}, the operand slot order). Piece j of column n sits at
+// piece j ^ f(n). Rows of 16 R bytes pack 16 / R columns into one 256-byte
+// bank line; f(n) = (n / (16 / R)) mod R then gives the 16 columns of a pass
+// 16 distinct 16-byte bank groups.
+template <int R>
+__device__ __forceinline__ int cm_off(int n, int j) {
+    constexpr int PER = 16 / R;
+    return n * (16 * R) + 16 * (j ^ ((n / PER) & (R - 1)));
+}
 
 // Work unit of the recurrence: one segment of one sequence (a whole sequence
 // when the prefill is not split).
@@ -514,25 +613,31 @@ enum : int {
                        // results to the segment buffers
 };
 
+// Registers a helper wave loads one step ahead for its output rows.
+template <int KS>
+struct HelperRows {
+    bf16x8 q[KS];     // q rows as row operands
+    bf16x8 pr[2];     // P rows as row operands (k-steps over the 64 tokens)
+    f32x4 sz;         // exp(gamma) rq of its 4 rows
+};
+
 template <int DK, int NW, int MODE>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64 * NW + 256)
 prefill_recurrent_kernel(PrefillParams p) {
-    using S = RecShape<DK, NW>;
-    constexpr int NT = S::NT, NV = S::NV, KS = S::KS, MT = S::MT;
+    using S = RecShape<DK, NW, MODE>;
+    constexpr bool OUT = S::OUT;
+    constexpr int NV = S::NV, NA = S::NA, KS = S::KS, MT = S::MT;
     constexpr int SV = S::SV, SO = S::SO;
     constexpr int KQ = S::KQ, TP = S::TP, VV = S::VV, SCN = S::SCN;
-    constexpr bool OUT = MODE == kModeOutput;
-    __shared__ __align__(16) uint16_t sK[kC * DK];   // swizzled, see kq_swz
-    __shared__ __align__(16) uint16_t sQ[OUT ? kC * DK : 8];
-    __shared__ __align__(16) uint16_t sT[kC * kC];   // swizzled, see tp_off
-    __shared__ __align__(16) uint16_t sP[OUT ? kC * kC : 8];
-    __shared__ __align__(16) uint16_t sV[kC * SV];
-    __shared__ __align__(16) uint16_t sO[OUT ? kC * SO : 8];
-    __shared__ __align__(16) float sSc[kScRows * kC];
+    __shared__ __align__(16) unsigned char lds[S::BYTES];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
     const int g4 = lane >> 4, l16 = lane & 15;
+    const bool helper = tid >= NA;
+    // index within the role, in a scalar register (wave-uniform addresses
+    // and buffer resources derived from it stay scalar)
+    const int wave = __builtin_amdgcn_readfirstlane((helper ? tid - NA : tid) >> 6);
     // blockIdx.x -> (key head, value head in its group, column group), key
     // head fastest so that the workgroups sharing one key head's q/k rows sit
     // on the same XCD (workgroups are dealt to the 8 XCDs round robin).
@@ -559,144 +664,224 @@ prefill_recurrent_kernel(PrefillParams p) {
     const int ncg = p.dv / NV;
     const bool m_cols = !OUT && grp >= ncg;
     const int vcol0 = (m_cols ? grp - ncg : grp) * NV;
-    const int col = vcol0 + wave * 16 + l16;    // this lane's column (value or transition)
+    const int nch = c1 - c0;
 
-    // fp32 master state: H[mu][i] = H[16 mu + 4 g + i][col]
-    f32x4 H[MT];
-    const float* init = nullptr;
-    if (OUT) {
-        // A split sequence starts every segment, the first included, from the
-        // chained initial states: the source slot is then read only by pass 2,
-        // before the last segment may overwrite it in place.
-        if (sg.split) init = p.sh + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
-        else if (ssl >= 0) init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
-    }
-    if (init != nullptr) {
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) H[mu][i] = init[(16 * mu + 4 * g4 + i) * p.dv + col];
-    } else {
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) H[mu][i] = (m_cols && 16 * mu + 4 * g4 + i == col) ? 1.f : 0.f;
-    }
+    auto tile16 = [&](int off, int b, int size) {
+        return reinterpret_cast<uint16_t*>(lds + off + b * size);
+    };
 
-    // register staging of one chunk's operands (the next chunk is fetched
-    // while the current one is computed)
-    u32x4 rK[KQ], rQ[KQ], rT[TP], rP[TP], rV[VV], rS[SCN];
+    // ---------------- helper role: staging ----------------
+    // Every helper step issues the same loads and stores with no branch
+    // around them (the counts of outstanding memory operations then stay
+    // exact, so a wait covers only what it needs): chunk indices are clamped
+    // into the segment, and rows past a chunk's end or a disabled store fall
+    // outside a buffer resource's range, where loads return zero and stores
+    // are dropped.
+    const unsigned kq_row = static_cast<unsigned>(p.hk) * DK;   // elements between token rows
+    const unsigned v_row = static_cast<unsigned>(p.hv) * p.dv;
+    const int htid = tid - NA;
+    constexpr unsigned kOff = 0x80000000u;      // offset past every range
+    u32x4 rK[KQ], rT[TP], rV[VV], rS[SCN];
+    auto chunk_len = [&](int c) { return min(kC, te - (tb + (c - c0) * kC)); };
     auto fetch = [&](int c) {
         const int t0 = tb + (c - c0) * kC;
-        const int len = min(kC, te - t0);
+        const int len = chunk_len(c);
+        const rsrc_t kr = make_rsrc(p.k + (static_cast<size_t>(t0) * p.hk + j) * DK, rows_bytes(len, kq_row, DK));
 #pragma unroll
         for (int m = 0; m < KQ; ++m) {
-            const int idx = tid + NT * m;
+            const int idx = htid + S::NB * m;
             const int r = idx / (DK / 8), c8 = idx % (DK / 8);
-            rK[m] = u32x4{0u, 0u, 0u, 0u};
-            rQ[m] = u32x4{0u, 0u, 0u, 0u};
-            if (r < len) {
-                const size_t off = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + c8 * 8;
-                rK[m] = *reinterpret_cast<const u32x4*>(p.k + off);
-                if (OUT) rQ[m] = *reinterpret_cast<const u32x4*>(p.q + off);
-            }
+            rK[m] = buf_load16(kr, 2u * (r * kq_row + c8 * 8));
         }
         const uint16_t* TPg = p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC);
 #pragma unroll
-        for (int m = 0; m < TP; ++m) {
-            const int idx = tid + NT * m;
-            rT[m] = *reinterpret_cast<const u32x4*>(TPg + 8 * idx);
-            if (OUT) rP[m] = *reinterpret_cast<const u32x4*>(TPg + kC * kC + 8 * idx);
-        }
+        for (int m = 0; m < TP; ++m) rT[m] = *at_bytes<u32x4>(TPg, 16u * (htid + S::NB * m));
+        const rsrc_t vr = make_rsrc(p.v + (static_cast<size_t>(t0) * p.hv + h) * p.dv + vcol0,
+                                    m_cols ? 0u : rows_bytes(len, v_row, NV));
 #pragma unroll
         for (int m = 0; m < VV; ++m) {
-            const int idx = tid + NT * m;
+            const int idx = htid + S::NB * m;
             const int r = idx / (NV / 8), c8 = idx % (NV / 8);
-            rV[m] = u32x4{0u, 0u, 0u, 0u};
-            if (r < len && !m_cols)
-                rV[m] = *reinterpret_cast<const u32x4*>(p.v + (static_cast<size_t>(t0 + r) * p.hv + h) * p.dv + vcol0 + 8 * c8);
+            rV[m] = buf_load16(vr, idx < S::VP ? 2u * (r * v_row + 8 * c8) : kOff);
         }
-        const float* SCg = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScRows * kC);
+        const rsrc_t sr = make_rsrc(p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScRows * kC), 16u * S::SCP);
 #pragma unroll
         for (int m = 0; m < SCN; ++m) {
-            const int idx = tid + NT * m;
-            if (idx < kScRows * kC / 4) rS[m] = *reinterpret_cast<const u32x4*>(SCg + 4 * idx);
+            const int idx = htid + S::NB * m;
+            rS[m] = buf_load16(sr, idx < S::SCP ? 16u * idx : kOff);
         }
     };
-    auto stage = [&]() {
+    auto stage = [&](int b) {
+        uint16_t* sK = tile16(S::L_K, b, S::SZ_K);
+        uint16_t* sT = tile16(S::L_T, b, S::SZ_T);
+        uint16_t* sV = tile16(S::L_V, b, S::SZ_V);
+        float* sSc = reinterpret_cast<float*>(lds + S::L_SC + b * S::SZ_SC);
 #pragma unroll
         for (int m = 0; m < KQ; ++m) {
-            const int idx = tid + NT * m;
+            const int idx = htid + S::NB * m;
             const int r = idx / (DK / 8), c8 = idx % (DK / 8);
             *reinterpret_cast<u32x4*>(sK + kq_off<DK, false>(r, c8 * 8)) = rK[m];
-            if (OUT) *reinterpret_cast<u32x4*>(sQ + kq_off<DK, true>(r, c8 * 8)) = rQ[m];
         }
 #pragma unroll
         for (int m = 0; m < TP; ++m) {
-            const int idx = tid + NT * m;
+            const int idx = htid + S::NB * m;
             const int r = idx / 8, c8 = idx % 8;
             *reinterpret_cast<u32x4*>(sT + tp_off<false>(r, c8 * 8)) = rT[m];
-            if (OUT) *reinterpret_cast<u32x4*>(sP + tp_off<true>(r, c8 * 8)) = rP[m];
         }
+        if (!m_cols) {
 #pragma unroll
-        for (int m = 0; m < VV; ++m) {
-            const int idx = tid + NT * m;
-            const int r = idx / (NV / 8), c8 = idx % (NV / 8);
-            *reinterpret_cast<u32x4*>(sV + r * SV + c8 * 8) = rV[m];
+            for (int m = 0; m < VV; ++m) {
+                const int idx = htid + S::NB * m;
+                const int r = idx / (NV / 8), c8 = idx % (NV / 8);
+                if (idx < S::VP) *reinterpret_cast<u32x4*>(sV + r * SV + c8 * 8) = rV[m];
+            }
         }
 #pragma unroll
         for (int m = 0; m < SCN; ++m) {
-            const int idx = tid + NT * m;
-            if (idx < kScRows * kC / 4) *reinterpret_cast<u32x4*>(sSc + 4 * idx) = rS[m];
+            const int idx = htid + S::NB * m;
+            if (idx < S::SCP) *reinterpret_cast<u32x4*>(sSc + 4 * idx) = rS[m];
         }
     };
-    // write the staged output tile of the chunk starting at token t0o
-    auto store_o = [&](int t0o, int leno) {
+
+    // ---------------- helper role: outputs ----------------
+    // helper wave w owns chunk rows [16 w, 16 w + 16)
+    // q and P rows come as row-operand fragments written by the intra-chunk
+    // kernel: one contiguous kilobyte per (row tile, k-step)
+    auto fetch_rows = [&](int c, HelperRows<KS>& hr) {
+        const uint16_t* Qf = p.qf + (static_cast<size_t>(c) * p.hk + j) * (kC * DK);
 #pragma unroll
-        for (int m = 0; m < VV; ++m) {
-            const int idx = tid + NT * m;
+        for (int ks = 0; ks < KS; ++ks) hr.q[ks] = *at_bytes<bf16x8>(Qf, 16u * ((wave * KS + ks) * 64 + lane));
+        // (the second k-step of P is all zero for rows below 32 and is then not used)
+        const uint16_t* Pf = p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC) + kC * kC;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) hr.pr[ks] = *at_bytes<bf16x8>(Pf, 16u * ((wave * 2 + ks) * 64 + lane));
+        const float* SCg = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScRows * kC);
+        hr.sz = *at_bytes<f32x4>(SCg, 4u * (kScZ * kC + 16 * wave + 4 * g4));
+    };
+    // outputs of the helper's rows of a chunk from buffer b, as bf16 row
+    // pieces in registers
+    constexpr int OP = 16 * NV / 8;               // 16-byte pieces in the wave's 16 x NV tile
+    constexpr int OPL = (OP + 63) / 64;           // per lane
+    auto emit_rows = [&](int b, const HelperRows<KS>& hr, u32x4 (&ov)[OPL]) {
+        const unsigned char* sH = lds + S::L_H + b * S::SZ_H;
+        const unsigned char* sU = lds + S::L_U + b * S::SZ_U;
+        f32x4 acc[NW];
+#pragma unroll
+        for (int ct = 0; ct < NW; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Z = Q H (contraction over dk), H read back column-major: lane
+        // (g, column) takes features 32 ks + 8 g .. +7, as its q fragment
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 hbv[NW];
+#pragma unroll
+            for (int ct = 0; ct < NW; ++ct)
+                hbv[ct] = *reinterpret_cast<const bf16x8*>(sH + cm_off<DK / 8>(16 * ct + l16, 4 * ks + g4));
+#pragma unroll
+            for (int ct = 0; ct < NW; ++ct) acc[ct] = mfma16(hr.q[ks], hbv[ct], acc[ct]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NW; ++ct) acc[ct] *= hr.sz;
+        // + P U (contraction over the chunk's tokens)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks == 1 && wave < 2) break;
+            bf16x8 ubv[NW];
+#pragma unroll
+            for (int ct = 0; ct < NW; ++ct)
+                ubv[ct] = *reinterpret_cast<const bf16x8*>(sU + cm_off<8>(16 * ct + l16, 4 * ks + g4));
+#pragma unroll
+            for (int ct = 0; ct < NW; ++ct) acc[ct] = mfma16(hr.pr[ks], ubv[ct], acc[ct]);
+        }
+        // through the wave's own LDS tile to 16-byte row stores
+        uint16_t* sO = reinterpret_cast<uint16_t*>(lds + S::L_O) + wave * 16 * SO;
+#pragma unroll
+        for (int ct = 0; ct < NW; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sO[(4 * g4 + i) * SO + 16 * ct + l16] = f32_to_bf16(acc[ct][i]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+        for (int m = 0; m < OPL; ++m) {
+            const int idx = lane + 64 * m;
             const int r = idx / (NV / 8), c8 = idx % (NV / 8);
-            if (r < leno)
-                *reinterpret_cast<u32x4*>(p.o + (static_cast<size_t>(t0o + r) * p.hv + h) * p.dv + vcol0 + 8 * c8) =
-                    *reinterpret_cast<const u32x4*>(sO + r * SO + c8 * 8);
+            ov[m] = *reinterpret_cast<const u32x4*>(sO + (idx < OP ? r * SO + c8 * 8 : 0));
+        }
+    };
+    // store the rows emitted for chunk c (last in a helper step: no wait of
+    // the step then queues behind the stores); nothing is stored when `live`
+    // is false
+    auto store_rows = [&](int c, bool live, const u32x4 (&ov)[OPL]) {
+        const int t0 = tb + (c - c0) * kC;
+        const int len = chunk_len(c) - 16 * wave;   // rows of this wave's block inside the chunk
+        const rsrc_t orr = make_rsrc(p.o + (static_cast<size_t>(t0 + 16 * wave) * p.hv + h) * p.dv + vcol0,
+                                     live ? rows_bytes(len, v_row, NV) : 0u);
+#pragma unroll
+        for (int m = 0; m < OPL; ++m) {
+            const int idx = lane + 64 * m;
+            const int r = idx / (NV / 8), c8 = idx % (NV / 8);
+            buf_store16(ov[m], orr, idx < OP ? 2u * (r * v_row + 8 * c8) : kOff);
         }
     };
 
-    if (c0 < c1) fetch(c0);
-    int prev_t0 = 0, prev_len = 0;
-    for (int c = c0; c < c1; ++c) {
-        const int t0 = tb + (c - c0) * kC;
-        const int len = min(kC, te - t0);
-        lds_barrier();                   // previous chunk's LDS reads and sO writes are done
-        if (OUT && prev_len > 0) store_o(prev_t0, prev_len);
-        stage();
-        lds_barrier();
-        if (c + 1 < c1) fetch(c + 1);    // in flight while this chunk is computed
-
-        // X = K H and Z = Q H  (contraction over dk). k-step outer, row tile
-        // inner: each step reads its operands first and then issues its
-        // independent MFMAs, so LDS latency overlaps the matrix pipe.
+    // ---------------- compute role ----------------
+    const int col = vcol0 + wave * 16 + l16;    // this lane's column (value or transition)
+    // fp32 master state: H[mu][i] = H[16 mu + 4 g + i][col]
+    f32x4 H[MT];
+    if (!helper) {
+        const float* init = nullptr;
+        if (OUT) {
+            // A split sequence starts every segment, the first included, from
+            // the chained initial states: the source slot is then read only by
+            // the chain pass, before the last segment may overwrite it in place.
+            if (sg.split) init = p.sh + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+            else if (ssl >= 0) init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+        }
+        if (init != nullptr) {
+#pragma unroll
+            for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) H[mu][i] = init[(16 * mu + 4 * g4 + i) * p.dv + col];
+        } else {
+#pragma unroll
+            for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) H[mu][i] = (m_cols && 16 * mu + 4 * g4 + i == col) ? 1.f : 0.f;
+        }
+    }
+    auto chunk = [&](int b) {
+        const uint16_t* sK = tile16(S::L_K, b, S::SZ_K);
+        const uint16_t* sT = tile16(S::L_T, b, S::SZ_T);
+        const uint16_t* sV = tile16(S::L_V, b, S::SZ_V);
+        const float* sSc = reinterpret_cast<const float*>(lds + S::L_SC + b * S::SZ_SC);
         bf16x8 hb[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) hb[ks] = pack8(H[2 * ks], H[2 * ks + 1]);
-        f32x4 X[4], Z[4];
+        // X = K H (contraction over dk); k-step outer so that each step's
+        // operand reads overlap the previous step's MFMAs
+        f32x4 X[4];
 #pragma unroll
-        for (int tau = 0; tau < 4; ++tau) {
-            X[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Z[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int tau = 0; tau < 4; ++tau) X[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 ak[4], aq[4];
+            bf16x8 ak[4];
 #pragma unroll
-            for (int tau = 0; tau < 4; ++tau) {
-                ak[tau] = kq_pair<DK, false>(sK, 16 * tau + l16, 32 * ks, g4);
-                if (OUT) aq[tau] = kq_pair<DK, true>(sQ, 16 * tau + l16, 32 * ks, g4);
-            }
+            for (int tau = 0; tau < 4; ++tau) ak[tau] = kq_pair<DK, false>(sK, 16 * tau + l16, 32 * ks, g4);
 #pragma unroll
-            for (int tau = 0; tau < 4; ++tau) {
-                X[tau] = mfma16(ak[tau], hb[ks], X[tau]);
-                if (OUT) Z[tau] = mfma16(aq[tau], hb[ks], Z[tau]);
+            for (int tau = 0; tau < 4; ++tau) X[tau] = mfma16(ak[tau], hb[ks], X[tau]);
+        }
+        if (OUT) {
+            // publish the chunk's initial state for the helpers' Q H, column
+            // by column in natural feature order (the helpers' q fragments
+            // hold 8 consecutive features per lane): rows 16 mu + 4 g .. +3
+            // are the half (g & 1) of 16-byte piece 2 mu + (g >> 1)
+            unsigned char* sH = lds + S::L_H + b * S::SZ_H;
+            const int n = 16 * wave + l16;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 w = __builtin_bit_cast(u32x4, hb[ks]);
+                *reinterpret_cast<u32x2*>(sH + cm_off<DK / 8>(n, 4 * ks + (g4 >> 1)) + 8 * (g4 & 1)) = u32x2{w.x, w.y};
+                *reinterpret_cast<u32x2*>(sH + cm_off<DK / 8>(n, 4 * ks + 2 + (g4 >> 1)) + 8 * (g4 & 1)) = u32x2{w.z, w.w};
             }
         }
         // Y = diag(beta) (V - diag(exp(gamma) rk) X)
@@ -706,7 +891,7 @@ prefill_recurrent_kernel(PrefillParams p) {
             const int r0 = 16 * tau + 4 * g4;
             const f32x4 sx = *reinterpret_cast<const f32x4*>(sSc + kScX * kC + r0);
             const f32x4 sb = *reinterpret_cast<const f32x4*>(sSc + kScBeta * kC + r0);
-            const f32x4 vv = lds_tr4_f32(sV, SV, 16 * tau, wave * 16, g4, l16);
+            const f32x4 vv = m_cols ? f32x4{0.f, 0.f, 0.f, 0.f} : lds_tr4_f32(sV, SV, 16 * tau, wave * 16, g4, l16);
             Y[tau] = sb * (vv - sx * X[tau]);
         }
         const bf16x8 yb0 = pack8(Y[0], Y[1]), yb1 = pack8(Y[2], Y[3]);
@@ -718,18 +903,9 @@ prefill_recurrent_kernel(PrefillParams p) {
             if (tau >= 2) U[tau] = mfma16(tp_pair<false>(sT, 16 * tau + l16, 32, g4), yb1, U[tau]);
         }
         if (OUT) {
-            // O = diag(exp(gamma) rq) Z + P U  -> staged in LDS as bf16
-            const bf16x8 ub0 = pack8(U[0], U[1]), ub1 = pack8(U[2], U[3]);
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau) {
-                f32x4 O = mfma16(tp_pair<true>(sP, 16 * tau + l16, 0, g4), ub0, f32x4{0.f, 0.f, 0.f, 0.f});
-                if (tau >= 2) O = mfma16(tp_pair<true>(sP, 16 * tau + l16, 32, g4), ub1, O);
-                const int r0 = 16 * tau + 4 * g4;
-                const f32x4 sz = *reinterpret_cast<const f32x4*>(sSc + kScZ * kC + r0);
-                O += sz * Z[tau];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sO[(r0 + i) * SO + wave * 16 + l16] = f32_to_bf16(O[i]);
-            }
+            unsigned char* sU = lds + S::L_U + b * S::SZ_U;
+            *reinterpret_cast<bf16x8*>(sU + cm_off<8>(16 * wave + l16, g4)) = pack8(U[0], U[1]);
+            *reinterpret_cast<bf16x8*>(sU + cm_off<8>(16 * wave + l16, 4 + g4)) = pack8(U[2], U[3]);
         }
         // H' = exp(gamma_last) H + K^T diag(rk exp(gamma_last - gamma)) U
         f32x4 DU[4];
@@ -754,12 +930,50 @@ prefill_recurrent_kernel(PrefillParams p) {
                 for (int m = 0; m < 4 && m0 + m < MT; ++m) H[m0 + m] = mfma16(at[m], db, H[m0 + m]);
             }
         }
-        prev_t0 = t0;
-        prev_len = len;
-    }
-    if (OUT) {
+    };
+
+    // ---------------- the pipeline ----------------
+    // step s: compute waves run chunk s (buffer s & 1); helpers stage chunk
+    // s + 1 into buffer (s + 1) & 1 and emit the outputs of chunk s - 1
+    // (buffer (s - 1) & 1), whose q / P rows they loaded during step s - 1.
+    // The two roles run separate loops with the same number of barriers.
+    // An empty segment (a zero-length sequence) skips the pipeline entirely:
+    // no wave meets a barrier and the state is only carried to the slot.
+    const int steps = nch == 0 ? 0 : OUT ? nch + 1 : nch;
+    if (helper) {
+        if (steps == 0) return;
+        HelperRows<KS> rows0, rows1 = {};   // rows1 feeds the first step's discarded outputs
+        fetch(c0);
+        stage(0);
         lds_barrier();
-        if (prev_len > 0) store_o(prev_t0, prev_len);
+        u32x4 ov[OPL];
+        auto hstep = [&](int s, int b, HelperRows<KS>& cur, HelperRows<KS>& nxt) {
+            fetch(min(c0 + s + 1, c1 - 1));
+            if (OUT) {
+                fetch_rows(min(c0 + s, c1 - 1), nxt);
+                emit_rows(b ^ 1, cur, ov);
+            }
+            stage(b ^ 1);             // past the last chunk: a harmless copy into an unused buffer
+            if (OUT) store_rows(c0 + max(s - 1, 0), s >= 1, ov);
+            lds_barrier();
+        };
+        for (int s = 0; s < steps; s += 2) {
+            hstep(s, 0, rows1, rows0);
+            if (s + 1 < steps) hstep(s + 1, 1, rows0, rows1);
+        }
+        return;
+    }
+    if (steps > 0) lds_barrier();
+    for (int s = 0; s < steps; s += 2) {
+        if (s < nch) chunk(0);
+        lds_barrier();
+        if (s + 1 < steps) {
+            if (s + 1 < nch) chunk(1);
+            lds_barrier();
+        }
+    }
+
+    if (OUT) {
         if (!sg.last) return;               // a middle segment's end state is the next one's start (pass 2)
         float* out = p.pool + (static_cast<size_t>(dsl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
 #pragma unroll
@@ -898,9 +1112,9 @@ template <int DK, int MODE>
 void launch_recurrence(const PrefillParams& p, int nw, int groups, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(p.hv * groups), static_cast<unsigned>(p.num_segs));
     switch (nw) {
-        case 1: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 1, MODE>), grid, dim3(64), 0, s, p); break;
-        case 2: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 2, MODE>), grid, dim3(128), 0, s, p); break;
-        default: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 4, MODE>), grid, dim3(256), 0, s, p); break;
+        case 1: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 1, MODE>), grid, dim3(64 + 256), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 2, MODE>), grid, dim3(128 + 256), 0, s, p); break;
+        default: hipLaunchKernelGGL((prefill_recurrent_kernel<DK, 4, MODE>), grid, dim3(256 + 256), 0, s, p); break;
     }
 }
 
@@ -950,6 +1164,7 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
     p.dst = a->dst_slots;
     p.err = a->err_flag;
     p.tp = reinterpret_cast<uint16_t*>(ws + plan.off_tp);
+    p.qf = reinterpret_cast<uint16_t*>(ws + plan.off_qf);
     p.sc = reinterpret_cast<float*>(ws + plan.off_sc);
     p.seg_off = reinterpret_cast<const int32_t*>(ws + plan.off_seg_offsets);
     p.seg_off_w = reinterpret_cast<int32_t*>(ws + plan.off_seg_offsets);
