@@ -67,6 +67,55 @@ static bool prefill_dims_supported(int32_t dk, int32_t dv) {
     return (dk == 32 || dk == 64 || dk == 128) && (dv == 16 || dv == 32 || dv == 64 || dv == 128);
 }
 
+// Segment length of the sequence split, from a cost model of the three
+// recurrence passes: a pass takes whole rounds of kNumCUs workgroups (one
+// resident per CU), each round as many steps as its longest chain. Costs per
+// step are measured cycle counts of the MI355X kernels: state pass 2800 (per
+// chunk), output pass 3800 (per chunk, one extra step), chain pass 9700 (per
+// segment hop). Returns 0 (no split) when one pass is estimated fastest.
+int32_t choose_seg_len(const int32_t* cu, int32_t n, int32_t hv, int32_t dk, int32_t dv) {
+    constexpr double kState = 2800, kOut = 3800, kHop = 9700;
+    const int64_t w_out = static_cast<int64_t>(hv) * (dv / 64);          // workgroups per segment, output pass
+    const int64_t w_state = static_cast<int64_t>(hv) * (dv / 64 + dk / 64);  // state pass
+    auto pass = [](int64_t wg_steps, int64_t longest) {
+        // whole rounds of kNumCUs workgroups, each at least `longest` steps
+        const double rounds = std::ceil(static_cast<double>(wg_steps) / (static_cast<double>(kNumCUs) * longest));
+        return std::max(1.0, rounds) * longest;
+    };
+    auto cost = [&](int64_t L) {
+        int64_t out_steps = 0, state_steps = 0, longest = 0, hops = 0;
+        for (int32_t i = 0; i < n; ++i) {
+            const int64_t c = (static_cast<int64_t>(cu[i + 1]) - cu[i] + 63) / 64;
+            if (c == 0) continue;
+            const int64_t nseg = (L == 0 || c <= L) ? 1 : (c + L - 1) / L;
+            const int64_t seg = (nseg == 1) ? c : L;
+            out_steps += (c + nseg) * w_out;
+            if (nseg > 1) state_steps += (nseg - 1) * L * w_state;
+            longest = std::max(longest, seg + 1);
+            hops = std::max(hops, nseg - 1);
+        }
+        if (longest == 0) return 0.0;
+        double t = kOut * pass(out_steps, longest);
+        if (hops > 0) t += kState * pass(state_steps, L) + kHop * static_cast<double>(hops);
+        return t;
+    };
+    // candidates: the longest sequence cut into k equal segments, k = 2 .. 32
+    int64_t cmax = 0;
+    for (int32_t i = 0; i < n; ++i) cmax = std::max<int64_t>(cmax, (static_cast<int64_t>(cu[i + 1]) - cu[i] + 63) / 64);
+    int32_t best = 0;
+    double best_cost = cost(0);
+    for (int64_t k = 2; k <= 32; ++k) {
+        const int64_t L = (cmax + k - 1) / k;
+        if (L < 8) break;
+        const double c = cost(L);
+        if (c < 0.97 * best_cost) {
+            best = static_cast<int32_t>(L);
+            best_cost = c;
+        }
+    }
+    return best;
+}
+
 int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* plan) {
     const char* fn = "gdn_prefill_chunked";
     if (pool == nullptr || a == nullptr) return fail(GDN_E_INVALID, "gdn_prefill_chunked: NULL pool or args");
@@ -102,14 +151,9 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     if (chunks * a->num_v_heads > INT32_MAX / 2)
         return fail(GDN_E_INVALID, "gdn_prefill_chunked: too many chunks");
     plan->num_chunks = static_cast<int32_t>(chunks);
-    // Split long sequences when the longest chunk chain is more than twice the
-    // average per-CU load of one pass (the recurrence runs one workgroup per
-    // (sequence, value head, 64 value columns)).
-    const int64_t wgs_per_seq = static_cast<int64_t>(a->num_v_heads) * ((a->dv + 63) / 64);
-    const int64_t avg_load = (chunks * wgs_per_seq + kNumCUs - 1) / kNumCUs;
     // (the transition columns and the chain pass work in 64-column groups)
     const bool can_split = a->dk >= 64 && a->dv >= 64;
-    plan->seg_len = (can_split && max_chunks > kSegChunks && max_chunks > 2 * avg_load) ? kSegChunks : 0;
+    plan->seg_len = can_split ? choose_seg_len(a->cu_seqlens_host, n, a->num_v_heads, a->dk, a->dv) : 0;
     int64_t segs = 0;
     for (int32_t i = 0; i < n; ++i) {
         const int64_t c = (static_cast<int64_t>(a->cu_seqlens_host[i + 1]) - a->cu_seqlens_host[i] + 63) / 64;

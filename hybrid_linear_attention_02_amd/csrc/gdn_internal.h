@@ -34,9 +34,9 @@ int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream);
 // computed for all segments at once, chained across segments, and the
 // segments then run their outputs in parallel from their true initial
 // states. It costs about twice the work of one pass, so it is used only when
-// one pass would leave most of the chip idle.
-constexpr int kSegChunks = 16;    // chunks per segment when splitting
+// one pass would leave most of the chip idle; choose_seg_len picks the length.
 constexpr int kNumCUs = 256;      // MI355X compute units
+int32_t choose_seg_len(const int32_t* cu_host, int32_t n, int32_t hv, int32_t dk, int32_t dv);
 
 struct PrefillPlan {
     int32_t num_chunks = 0;       // sum over sequences of ceil(len / 64)
