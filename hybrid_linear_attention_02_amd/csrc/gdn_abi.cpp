@@ -171,8 +171,6 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     off = up(off + sizeof(int32_t) * static_cast<size_t>(n + 1));
     plan->off_tp = off;
     off = up(off + 2ull * chunks * hv * 2 * 64 * 64);
-    plan->off_qf = off;
-    off = up(off + 2ull * chunks * static_cast<size_t>(a->num_k_heads) * 64 * dk);
     plan->off_sc = off;
     off = up(off + 4ull * chunks * hv * (5 * 64));
     plan->off_se = off;

@@ -44,8 +44,7 @@ struct PrefillPlan {
     int32_t num_segs = 0;         // total segments
     size_t off_chunk_offsets = 0; // int32 [N+1]: first chunk of each sequence
     size_t off_seg_offsets = 0;   // int32 [N+1]: first segment of each sequence
-    size_t off_tp = 0;            // bf16 [chunks][HV][2][64 * 64]: T (row-major), P (row-operand fragments)
-    size_t off_qf = 0;            // bf16 [chunks][HK][64 * dk]: q rows as row-operand fragments
+    size_t off_tp = 0;            // bf16 [chunks][HV][2][64 * 64]: T and P as row-operand fragments
     size_t off_sc = 0;            // float [chunks][HV][5][64]: per-token scale rows
     size_t off_se = 0;            // float [segs][HV][dk][dv]: local end state E (split only)
     size_t off_sm = 0;            // bf16 [segs][HV][2][dk][dk]: transition M, high then low part (split only)

@@ -80,8 +80,7 @@ struct PrefillParams {
     const int32_t* src;
     const int32_t* dst;
     int32_t* err;
-    uint16_t* tp;               // [chunks][HV][2][64 * 64] T (row-major), then P as row-operand fragments
-    uint16_t* qf;               // [chunks][HK][64 * DK] q rows as row-operand fragments
+    uint16_t* tp;               // [chunks][HV][2][64 * 64] T, then P, as row-operand fragments
     float* sc;                  // [chunks][HV][5][64]    scale rows
     int32_t* chunk_off_w;       // same buffer as chunk_off, written by the prep kernel
     const int32_t* seg_off;     // [N+1] device (workspace): first segment of each sequence
@@ -269,28 +268,6 @@ __device__ __forceinline__ bf16x8 kq_tr_pair(const uint16_t* buf, int row0, int 
     return as_bf16x8(w);
 }
 
-// T and P tiles (64 x 64 bf16, G = 16), read only as row operands. A row
-// fills half of the banks, so the 8 same-parity rows of a pass need distinct
-// granule offsets: per-row term 2 ((r >> 1) & 7). Group constant 2 (r >> 4),
-// plus 8 for P.
-template <bool IS_P>
-__device__ __forceinline__ int tp_off(int r, int col) {
-    const int swz = (2 * ((r >> 1) & 7)) ^ ((2 * (r >> 4) + (IS_P ? 8 : 0)) & 14);
-    return r * kC + 4 * ((col >> 2) ^ swz) + (col & 3);
-}
-
-template <bool IS_P>
-__device__ __forceinline__ bf16x8 tp_pair(const uint16_t* buf, int row, int base, int g4) {
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(buf + tp_off<IS_P>(row, base + 4 * g4));
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(buf + tp_off<IS_P>(row, base + 16 + 4 * g4));
-    u32x4 w;
-    w.x = lo.x;
-    w.y = lo.y;
-    w.z = hi.x;
-    w.w = hi.y;
-    return as_bf16x8(w);
-}
-
 // Workgroup barrier that orders LDS only. A plain __syncthreads() also waits
 // for every outstanding global load and store of the wave (the workgroup
 // release fence covers global memory), which would put a full memory round
@@ -336,12 +313,25 @@ __device__ __forceinline__ int find_seq(const int32_t* off, int n_seqs, int c) {
 // intra-chunk: one wave per (chunk, value head)
 // ---------------------------------------------------------------------------
 
+// fp32 16 x 16 x 16 product on the fp32 MFMA: acc += X Y, with X given with
+// one row per lane (lane (row, g) holds X[row][4 g + e]) and Y in accumulator
+// layout (lane (column, g) holds Y[4 g + e][column]). Step kk contracts
+// k = 4 g + kk, so both operands are read in place. Swapping the arguments
+// yields (X Y)^T in accumulator layout, i.e. X Y with one row per lane.
+__device__ __forceinline__ f32x4 mm16(f32x4 x, f32x4 y, f32x4 acc) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[kk], y[kk], acc, 0, 0, 0);
+    return acc;
+}
+
 template <int DK>
 __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     constexpr int KS = DK / 32;       // MFMA k-steps over dk
-    constexpr int SA = kC + 4;        // row stride of A^T in LDS (fp32)
-    __shared__ __align__(16) float sAt[kC * SA];   // sAt[s][r] = A[r][s]
-    __shared__ float sGam[kC], sBeta[kC], sRk[kC], sRq[kC];
+    constexpr int SD = 20;            // row stride (floats) of the 16 x 16 block tiles in LDS
+    __shared__ __align__(16) float sAd[4 * 16 * SD];   // diagonal blocks of A, row-major
+    __shared__ __align__(16) float sTc[4 * 16 * SD];   // diagonal blocks of T, column-major
+    __shared__ __align__(16) float sTr[4 * 16 * SD];   // diagonal blocks of T, row-major
+    __shared__ __align__(16) float sGam[kC], sBeta[kC], sRk[kC], sRq[kC];
 
     const int c = blockIdx.x;
     const int h = blockIdx.y;
@@ -358,8 +348,8 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     // raw k rows as row operands in natural feature order (a contraction
     // over dk may order its k slots freely, as long as both operands agree):
     // kr[tt][ks] = K[16 tt + l16][32 ks + 8 g .. +7]
-    // (q rows are loaded one 16-row tile at a time below, to keep the
-    // register footprint, and with it the wave count per SIMD, in check)
+    // (q rows are loaded one 16-row tile ahead below, to keep the register
+    // footprint in check)
     const auto load_rows = [&](const uint16_t* x, int tt, u32x4* dst) {
         const int r = 16 * tt + l16;
         const size_t base = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + 8 * g4;
@@ -381,9 +371,10 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         acc += __shfl_xor(acc, 32);
         return acc;
     };
-    u32x4 kr[4][KS];
+    u32x4 kr[4][KS], qn[KS];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) load_rows(p.k, tt, kr[tt]);
+    load_rows(p.q, 0, qn);
     // per-token g, beta; cumulative log-decay by an inclusive lane scan
     float gl = 0.f, bl = 0.f;
     if (lane < len) {
@@ -410,29 +401,24 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     }
     lds_barrier();
 
-    // Gram tiles on MFMA, one row tile at a time: A (strictly lower) -> LDS
-    // transposed; P -> workspace as row-operand fragments (computed as P^T,
-    // whose accumulator layout puts one P row in each lane). The q rows of
-    // tile tr also give their norms and, once per key head, go to the
-    // workspace as row-operand fragments.
+    // Gram tiles on MFMA with one row per lane (each product takes the
+    // column tile's k rows as its first operand): A (strictly lower), kept in
+    // registers off the diagonal and in LDS on it, and P, which goes to the
+    // workspace as row-operand fragments. The q rows of tile tr also give
+    // their norms.
     u32x4* Pf = reinterpret_cast<u32x4*>(p.tp + ((static_cast<size_t>(c) * p.hv + h) * 2 + 1) * (kC * kC));
-    u32x4* Qf = reinterpret_cast<u32x4*>(p.qf + (static_cast<size_t>(c) * p.hk + j) * (kC * DK));
-    const bool write_q = h % p.group == 0;
+    f32x4 ra[6];                               // A blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 #pragma unroll
     for (int tr = 0; tr < 4; ++tr) {
         u32x4 qr[KS];
-        load_rows(p.q, tr, qr);
-        if (write_q) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) Qf[(tr * KS + ks) * 64 + lane] = qr[ks];
-        }
-        {
-            const float sq = row_sumsq(qr);
-            const int r = 16 * tr + l16;
-            if (g4 == 0) sRq[r] = (r < len) ? p.scale / sqrtf(sq + p.eps) : 0.f;
-        }
-        lds_barrier();
-        f32x4 pt[4];                           // pt[ts][i] = P[16 tr + l16][16 ts + 4 g + i]
+        for (int ks = 0; ks < KS; ++ks) qr[ks] = qn[ks];
+        if (tr < 3) load_rows(p.q, tr + 1, qn);
+        const int r = 16 * tr + l16;           // this lane's row
+        const float rq = (r < len) ? p.scale / sqrtf(row_sumsq(qr) + p.eps) : 0.f;
+        if (g4 == 0) sRq[r] = rq;
+        const float gr = sGam[r], br = sBeta[r], rkr = sRk[r];
+        f32x4 pt[4];                           // pt[ts][e] = P[r][16 ts + 4 g + e]
 #pragma unroll
         for (int ts = 0; ts < 4; ++ts) {
             pt[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -441,32 +427,21 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const bf16x8 bk = as_bf16x8(kr[ts][ks]);
-                kk = mfma16(as_bf16x8(kr[tr][ks]), bk, kk);
+                kk = mfma16(bk, as_bf16x8(kr[tr][ks]), kk);
                 kq = mfma16(bk, as_bf16x8(qr[ks]), kq);
             }
-            // A[r][s]: row r = 16 tr + 4 g + i, column (lane) s
-            {
-                const int s = 16 * ts + l16;
-                const float gs = sGam[s], rks = sRk[s];
-                f32x4 a;
+            const f32x4 gs = *reinterpret_cast<const f32x4*>(sGam + 16 * ts + 4 * g4);
+            const f32x4 rks = *reinterpret_cast<const f32x4*>(sRk + 16 * ts + 4 * g4);
+            f32x4 a;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * tr + 4 * g4 + i;
-                    const float dec = (s < r) ? exp2_hw(sGam[r] - gs) : 0.f;
-                    a[i] = (s < r) ? sBeta[r] * dec * kk[i] * sRk[r] * rks : 0.f;
-                }
-                *reinterpret_cast<f32x4*>(sAt + s * SA + 16 * tr + 4 * g4) = a;
+            for (int e = 0; e < 4; ++e) {
+                const int sc = 16 * ts + 4 * g4 + e;
+                const float dec = (sc <= r) ? exp2_hw(gr - gs[e]) : 0.f;
+                a[e] = (sc < r) ? br * dec * kk[e] * rkr * rks[e] : 0.f;
+                pt[ts][e] = dec * kq[e] * rq * rks[e];
             }
-            // P[r][s]: row (lane) r = 16 tr + l16, column s = 16 ts + 4 g + i
-            {
-                const int r = 16 * tr + l16;
-                const float gr = sGam[r], rqr = sRq[r];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s = 16 * ts + 4 * g4 + i;
-                    pt[ts][i] = (s <= r) ? exp2_hw(gr - sGam[s]) * kq[i] * rqr * sRk[s] : 0.f;
-                }
-            }
+            if (ts == tr) *reinterpret_cast<f32x4*>(sAd + (16 * tr + l16) * SD + 4 * g4) = a;
+            else ra[tr * (tr - 1) / 2 + ts] = a;
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) Pf[(tr * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(pt[2 * ks], pt[2 * ks + 1]));
@@ -483,34 +458,70 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         scp[kScE * kC + lane] = exp2_hw(gam_last);
     }
 
-    // T = (I + A)^-1, right-looking: lane t owns column t of T. Step s fixes
-    // x_s and adds A[r][s] x_s to every later row r; only x_s's own update is
-    // on the serial chain. The address of column s of A is tied to x_{s-1}
-    // through an empty asm so one column is in flight at a time (otherwise
-    // the scheduler hoists every load and spills); the other waves on the
-    // SIMD cover the LDS latency.
-    float x[kC];
+    // T = (I + A)^-1, blocked by 16. The four diagonal blocks
+    // T_bb = (I + A_bb)^-1 are solved at once, lane group b taking block b,
+    // lane t of it column t, by forward substitution over the block's rows.
+    {
+        const int bb = g4, t = l16;
+        float x[16];
 #pragma unroll
-    for (int r = 0; r < kC; ++r) x[r] = 0.f;
+        for (int r = 0; r < 16; ++r) {
+            const float* arow = sAd + (16 * bb + r) * SD;
+            float acc = (r == t) ? 1.f : 0.f;
 #pragma unroll
-    for (int s = 0; s < kC; ++s) {
-        x[s] = ((s == lane) ? 1.f : 0.f) - x[s];
-        if (s == kC - 1) break;
-        int col_off = s * SA;
-        __asm__ volatile("" : "+v"(col_off) : "v"(x[s]));
-        const float* acol = sAt + col_off;
-        const float xs = x[s];
+            for (int s4 = 0; s4 < r; s4 += 4) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(arow + s4);
 #pragma unroll
-        for (int r4 = (s + 1) / 4; r4 < kC / 4; ++r4) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(acol + 4 * r4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (4 * r4 + e > s) x[4 * r4 + e] += a[e] * xs;
+                for (int e = 0; e < 4; ++e)
+                    if (s4 + e < r) acc -= av[e] * x[s4 + e];
+            }
+            x[r] = acc;
         }
-    }
-    uint16_t* Tg = p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC);
 #pragma unroll
-    for (int r = 0; r < kC; ++r) Tg[r * kC + lane] = f32_to_bf16(x[r]);
+        for (int r4 = 0; r4 < 16; r4 += 4)
+            *reinterpret_cast<f32x4*>(sTc + (16 * bb + t) * SD + r4) = f32x4{x[r4], x[r4 + 1], x[r4 + 2], x[r4 + 3]};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sTr[(16 * bb + r) * SD + t] = x[r];
+    }
+    lds_barrier();
+    // diagonal blocks in both operand layouts: C (lane = column) and R (lane = row)
+    f32x4 tc[3], trf[4];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+        if (bb < 3) tc[bb] = *reinterpret_cast<const f32x4*>(sTc + (16 * bb + l16) * SD + 4 * g4);
+        trf[bb] = *reinterpret_cast<const f32x4*>(sTr + (16 * bb + l16) * SD + 4 * g4);
+    }
+    // Off the diagonal, T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj), level by
+    // level on the fp32 MFMA; blocks used again later are kept in layout C,
+    // every block is produced in layout R for the output.
+    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 S;
+    S = mm16(ra[0], tc[0], z);                                    // A10 T00
+    const f32x4 t10c = -mm16(trf[1], S, z), t10r = -mm16(S, trf[1], z);
+    S = mm16(ra[2], tc[1], z);                                    // A21 T11
+    const f32x4 t21c = -mm16(trf[2], S, z), t21r = -mm16(S, trf[2], z);
+    S = mm16(ra[5], tc[2], z);                                    // A32 T22
+    const f32x4 t32r = -mm16(S, trf[3], z);
+    S = mm16(ra[2], t10c, mm16(ra[1], tc[0], z));                 // A20 T00 + A21 T10
+    const f32x4 t20c = -mm16(trf[2], S, z), t20r = -mm16(S, trf[2], z);
+    S = mm16(ra[5], t21c, mm16(ra[4], tc[1], z));                 // A31 T11 + A32 T21
+    const f32x4 t31r = -mm16(S, trf[3], z);
+    S = mm16(ra[5], t20c, mm16(ra[4], t10c, mm16(ra[3], tc[0], z)));   // A30 T00 + A31 T10 + A32 T20
+    const f32x4 t30r = -mm16(S, trf[3], z);
+
+    // T to the workspace as row-operand fragments (tau, ks) = rows 16 tau ..,
+    // k block 32 ks: blocks (tau, 2 ks) and (tau, 2 ks + 1); the two all-zero
+    // fragments (0, 1) and (1, 1) are not written
+    u32x4* Tf = reinterpret_cast<u32x4*>(p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC));
+    auto put = [&](int tau, int ks, f32x4 lo, f32x4 hi) {
+        Tf[(tau * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(lo, hi));
+    };
+    put(0, 0, trf[0], z);
+    put(1, 0, t10r, trf[1]);
+    put(2, 0, t20r, t21r);
+    put(2, 1, trf[2], z);
+    put(3, 0, t30r, t31r);
+    put(3, 1, t32r, trf[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -723,11 +734,7 @@ prefill_recurrent_kernel(PrefillParams p) {
             *reinterpret_cast<u32x4*>(sK + kq_off<DK, false>(r, c8 * 8)) = rK[m];
         }
 #pragma unroll
-        for (int m = 0; m < TP; ++m) {
-            const int idx = htid + S::NB * m;
-            const int r = idx / 8, c8 = idx % 8;
-            *reinterpret_cast<u32x4*>(sT + tp_off<false>(r, c8 * 8)) = rT[m];
-        }
+        for (int m = 0; m < TP; ++m) *reinterpret_cast<u32x4*>(sT + 8 * (htid + S::NB * m)) = rT[m];
         if (!m_cols) {
 #pragma unroll
             for (int m = 0; m < VV; ++m) {
@@ -745,12 +752,16 @@ prefill_recurrent_kernel(PrefillParams p) {
 
     // ---------------- helper role: outputs ----------------
     // helper wave w owns chunk rows [16 w, 16 w + 16)
-    // q and P rows come as row-operand fragments written by the intra-chunk
-    // kernel: one contiguous kilobyte per (row tile, k-step)
+    // q rows as row operands in natural feature order (lane (g, row) takes
+    // features 32 ks + 8 g .. +7, matching the published H); P rows come as
+    // row-operand fragments written by the intra-chunk kernel, one contiguous
+    // kilobyte per (row tile, k-step)
     auto fetch_rows = [&](int c, HelperRows<KS>& hr) {
-        const uint16_t* Qf = p.qf + (static_cast<size_t>(c) * p.hk + j) * (kC * DK);
+        const int t0 = tb + (c - c0) * kC;
+        const rsrc_t qr = make_rsrc(p.q + (static_cast<size_t>(t0) * p.hk + j) * DK, rows_bytes(chunk_len(c), kq_row, DK));
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) hr.q[ks] = *at_bytes<bf16x8>(Qf, 16u * ((wave * KS + ks) * 64 + lane));
+        for (int ks = 0; ks < KS; ++ks)
+            hr.q[ks] = __builtin_bit_cast(bf16x8, buf_load16(qr, 2u * ((16 * wave + l16) * kq_row + 32 * ks + 8 * g4)));
         // (the second k-step of P is all zero for rows below 32 and is then not used)
         const uint16_t* Pf = p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC) + kC * kC;
 #pragma unroll
@@ -895,12 +906,16 @@ prefill_recurrent_kernel(PrefillParams p) {
             Y[tau] = sb * (vv - sx * X[tau]);
         }
         const bf16x8 yb0 = pack8(Y[0], Y[1]), yb1 = pack8(Y[2], Y[3]);
-        // U = T Y   (T lower triangular: skip the all-zero upper k-step)
+        // U = T Y   (T lower triangular: skip the all-zero upper k-step); T
+        // is staged as row-operand fragments, one kilobyte each
+        auto tfrag = [&](int tau, int ks) {
+            return *reinterpret_cast<const bf16x8*>(sT + 8 * ((tau * 2 + ks) * 64 + lane));
+        };
         f32x4 U[4];
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
-            U[tau] = mfma16(tp_pair<false>(sT, 16 * tau + l16, 0, g4), yb0, f32x4{0.f, 0.f, 0.f, 0.f});
-            if (tau >= 2) U[tau] = mfma16(tp_pair<false>(sT, 16 * tau + l16, 32, g4), yb1, U[tau]);
+            U[tau] = mfma16(tfrag(tau, 0), yb0, f32x4{0.f, 0.f, 0.f, 0.f});
+            if (tau >= 2) U[tau] = mfma16(tfrag(tau, 1), yb1, U[tau]);
         }
         if (OUT) {
             unsigned char* sU = lds + S::L_U + b * S::SZ_U;
@@ -1164,7 +1179,6 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
     p.dst = a->dst_slots;
     p.err = a->err_flag;
     p.tp = reinterpret_cast<uint16_t*>(ws + plan.off_tp);
-    p.qf = reinterpret_cast<uint16_t*>(ws + plan.off_qf);
     p.sc = reinterpret_cast<float*>(ws + plan.off_sc);
     p.seg_off = reinterpret_cast<const int32_t*>(ws + plan.off_seg_offsets);
     p.seg_off_w = reinterpret_cast<int32_t*>(ws + plan.off_seg_offsets);
