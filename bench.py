@@ -182,6 +182,18 @@ def bench_decode(steps, warmup):
 
 
 def bench_prefill(reps=20, warmup=3):
+    """Chunked prefill of one 8192-token sequence from a zero state into slot 1.
+
+    Three timings of the same call (repeats are idempotent: zero initial state,
+    same destination):
+      * steady state (``value``): `reps` calls issued back to back between two
+        events, the host running ahead of the GPU as in a pipelined engine;
+      * graph replay: the call recorded once as a HIP graph and replayed `reps`
+        times (no host work inside the timed region; outputs checked equal to
+        the eager call's);
+      * latency: median of single calls, each synchronised, host marshalling
+        and planning included.
+    """
     import torch
     from hybrid_linear_attention_02_amd import gdn
     from hybrid_linear_attention_02_amd.workloads import chunked_prefill
@@ -200,31 +212,58 @@ def bench_prefill(reps=20, warmup=3):
     src = torch.tensor([-1], dtype=torch.int32, device="cuda")
     dst = torch.tensor([1], dtype=torch.int32, device="cuda")
     ws = None
+    call = lambda: gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src, dst, workspace=ws)
     for _ in range(warmup):
         ws = gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src, dst, workspace=ws)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    times = []
-    for _ in range(reps):
+    o_ref = o.clone()
+    s_ref = storage[1].clone()
+
+    def span(fn, n):
         a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src, dst, workspace=ws)
-        e.record(stream)
         torch.cuda.synchronize()
-        times.append(a.elapsed_time(e))
-    t = float(np.median(times)) * 1e-3
+        a.record()
+        for _ in range(n):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(e) / n * 1e-3
+
+    steady = span(call, reps)
+    lat = []
+    for _ in range(reps):
+        lat.append(span(call, 1))
+    latency = float(np.median(lat))
+
+    graph_s = None
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    o.zero_()
+    graph_s = span(graph.replay, reps)
+    graph_ok = bool(torch.equal(o, o_ref) and torch.equal(storage[1], s_ref))
+
     flops = T * prefill_flops_per_token(pw.HV, pw.dk, pw.dv)
-    tflops = flops / t / 1e12
+    tflops = flops / steady / 1e12
     pool.close()
     return {
         "workload": "chunked_prefill_bf16_t8192_hk16_hv32_128x128_c64",
-        "value": T / t, "unit": "tok/s", "ms": t * 1e3, "dtype": "bf16",
+        "value": T / steady, "unit": "tok/s", "ms": steady * 1e3, "dtype": "bf16",
+        "graph_ms": graph_s * 1e3, "graph_matches_eager": graph_ok,
+        "latency_ms": latency * 1e3,
+        "timing": "value: back-to-back calls (host overlapped); graph_ms: HIP-graph replay; "
+                  "latency_ms: one synchronised call including host marshalling and planning",
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
                      "scope": "whole gdn_prefill_chunked call (prep + intra-chunk + recurrence kernels)"},
         "algorithmic_gflop": flops / 1e9,
         "hbm_gbs_algorithmic": (T * prefill_bytes_per_token(pw.HK, pw.HV, pw.dk, pw.dv) + pw.HV * pw.dk * pw.dv * 4)
-        / t / 1e9,
+        / steady / 1e9,
     }
 
 
@@ -282,6 +321,46 @@ def cpu_baseline(per_req_bytes, repeats=8):
             "request_steps_per_s": req_steps / wall, "wall_s": wall}
 
 
+def run_counters(launches=5, copy_mib=128):
+    """Short run for hardware-counter passes (rocprofv3 --pmc FETCH_SIZE, then
+    WRITE_SIZE): `launches` eager batched-decode steps, then one plain device
+    copy of `copy_mib` MiB whose counter readings calibrate the decode ones
+    (bytes actually moved / bytes the counter reports)."""
+    import torch
+    from hybrid_linear_attention_02_amd import gdn
+    from hybrid_linear_attention_02_amd.workloads import batched_decode
+
+    wl = batched_decode(steps=launches)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    inputs = [(bf(t.q), bf(t.k), bf(t.v), dev(t.g), dev(t.beta)) for t in wl.steps]
+    storage = dev(wl.pool)
+    pool = gdn.gdn_state_pool_create(wl.num_slots, wl.HV, wl.dk, wl.dv, storage=storage)
+    pool.alloc(wl.num_slots)
+    keep = set(int(s) for s in wl.src)
+    for s in range(wl.num_slots):
+        if s not in keep:
+            pool.release(s)
+    dst = pool.alloc(wl.B)
+    src_t = torch.tensor(wl.src, dtype=torch.int32, device="cuda")
+    dst_t = torch.tensor(dst, dtype=torch.int32, device="cuda")
+    o = torch.empty((wl.B, wl.HV, wl.dv), dtype=torch.bfloat16, device="cuda")
+    for i in range(launches):
+        q, k, v, g, b = inputs[i]
+        gdn.gdn_decode_step(pool, q, k, v, g, b, o, src_t if i == 0 else dst_t, dst_t)
+    torch.cuda.synchronize()
+    n = copy_mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    c = torch.empty_like(a)
+    c.copy_(a)
+    torch.cuda.synchronize()
+    pool.close()
+    print(json.dumps({"decode_launches": launches,
+                      "decode_algorithmic_bytes_per_launch": wl.B * decode_bytes_per_request(wl.HK, wl.HV, wl.dk, wl.dv, 2),
+                      "copy_bytes_each_way": n * 4,
+                      "decode_kernel_source_sha256_16": _src_hash("gdn_decode.hip")}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +368,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="short decode + calibration-copy run for rocprofv3 counter passes; prints no bench line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the GDN state update shards over heads and requests with no "
@@ -296,6 +377,9 @@ def main():
         sys.exit(2)
     # The CPU baseline forks its worker processes before this process touches
     # the GPU.
+    if args.counters:
+        run_counters()
+        return
     cpu = None if args.no_cpu_baseline else cpu_baseline(decode_bytes_per_request(16, 32, 128, 128, 2))
     import torch
     if not torch.cuda.is_available():
