@@ -281,6 +281,44 @@ def _oracle_worker(args):
     return time.perf_counter() - t0
 
 
+def _oracle_prefill_worker(args):
+    os.environ["OMP_NUM_THREADS"] = "1"
+    (q, k, v, g, b, dk, dv, scale) = args
+    from oracle import bf16_bits_to_f64, recurrent_sequence
+    t0 = time.perf_counter()
+    recurrent_sequence(np.zeros((v.shape[1], dk, dv)), bf16_bits_to_f64(q), bf16_bits_to_f64(k),
+                       bf16_bits_to_f64(v), g, b, scale, 1e-6)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_prefill(tokens=8192):
+    """The fp64 oracle's token loop on the first `tokens` tokens of the
+    8192-token prefill workload, all 32 value heads, one process per key head
+    (at most the host's cores, 16 at most)."""
+    from concurrent.futures import ProcessPoolExecutor
+    from hybrid_linear_attention_02_amd.workloads import chunked_prefill
+
+    pw = chunked_prefill()
+    tk = pw.tokens
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16, pw.HK))
+    G = pw.HV // pw.HK
+    jobs = []
+    for js in np.array_split(np.arange(pw.HK), cores):
+        hv = np.concatenate([np.arange(j * G, (j + 1) * G) for j in js])
+        jobs.append((tk.q[:tokens, js], tk.k[:tokens, js], tk.v[:tokens, hv], tk.g[:tokens, hv],
+                     tk.beta[:tokens, hv], pw.dk, pw.dv, pw.dk ** -0.5))
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=cores) as ex:
+        per = list(ex.map(_oracle_prefill_worker, jobs))
+    wall = time.perf_counter() - t0
+    flop = tokens * pw.HV * 7 * pw.dk * pw.dv
+    return {"value": tokens / wall, "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {tokens} tokens of the 8192-token workload, all {pw.HV} value heads; fp64 token "
+                      f"loop, one process per key head group ({cores} processes); wall {wall:.1f} s",
+            "per_core_tok_s": float(np.mean([tokens * len(j[2][0]) / pw.HV / t for j, t in zip(jobs, per)])),
+            "fp64_gflops": flop / wall / 1e9}
+
+
 def cpu_baseline(per_req_bytes, repeats=8):
     """The fp64 oracle (as it stands) on the whole batched-decode workload --
     64 requests x 100 steps, run `repeats` times back to back so the timed CPU
@@ -302,9 +340,10 @@ def cpu_baseline(per_req_bytes, repeats=8):
         jobs.append((npool, lsrc, ldst, steps_part, wl.dk ** -0.5, repeats))
     t0 = time.perf_counter()
     with ProcessPoolExecutor(max_workers=cores) as ex:
-        list(ex.map(_oracle_worker, jobs))
+        per = list(ex.map(_oracle_worker, jobs))
     wall = time.perf_counter() - t0
     req_steps = wl.B * len(wl.steps) * repeats
+    per_core = float(np.mean([len(rows) * len(wl.steps) * repeats / t for rows, t in zip(groups, per)]))
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -318,7 +357,42 @@ def cpu_baseline(per_req_bytes, repeats=8):
             "sample": f"whole batched-decode workload (64 requests x 100 steps, 16/32 heads, 128x128) run "
                       f"{repeats} times; fp64 token loop in {cores} processes on {cpu_model or 'host CPU'}; "
                       f"{req_steps / wall:.1f} request-steps/s, wall {wall:.1f} s",
-            "request_steps_per_s": req_steps / wall, "wall_s": wall}
+            "request_steps_per_s": req_steps / wall, "wall_s": wall,
+            "per_core_request_steps_per_s": per_core,
+            "fp64_gflops": req_steps * wl.HV * 7 * wl.dk * wl.dv / wall / 1e9}
+
+
+def achievable():
+    """Measured denominators next to the nominal peaks: a 1 GiB device copy
+    (bytes read + written per second) and a bf16 8192^3 GEMM (torch.matmul)."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    c = torch.empty_like(a)
+    x = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    y = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+
+    def best(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+
+    tc = best(lambda: c.copy_(a))
+    tg = best(lambda: torch.matmul(x, y))
+    copy_gbs = 2 * n * 4 / tc / 1e9
+    gemm = 2 * 8192 ** 3 / tg / 1e12
+    del a, c, x, y
+    return {"copy_gbs": round(copy_gbs, 1), "copy_frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "gemm_bf16_tflops": round(gemm, 1), "gemm_frac_of_peak": round(gemm / BF16_PEAK_TFLOPS, 4),
+            "protocol": "best of 10: 1 GiB float32 device copy; torch.matmul of two 8192x8192 bf16 matrices"}
 
 
 def run_counters(launches=5, copy_mib=128):
@@ -355,6 +429,25 @@ def run_counters(launches=5, copy_mib=128):
     c.copy_(a)
     torch.cuda.synchronize()
     pool.close()
+    del a, c
+    # two calls of the 8192-token prefill (the second one is the one to read)
+    from hybrid_linear_attention_02_amd.workloads import chunked_prefill
+    pw = chunked_prefill()
+    tk = pw.tokens
+    pq, pk, pv, pg, pb = bf(tk.q), bf(tk.k), bf(tk.v), dev(tk.g), dev(tk.beta)
+    T = int(pw.cu_seqlens[-1])
+    po = torch.empty((T, pw.HV, pw.dv), dtype=torch.bfloat16, device="cuda")
+    pst = torch.zeros((pw.num_slots, pw.HV, pw.dk, pw.dv), dtype=torch.float32, device="cuda")
+    ppool = gdn.gdn_state_pool_create(pw.num_slots, pw.HV, pw.dk, pw.dv, storage=pst)
+    ppool.alloc(pw.num_slots)
+    pcu = dev(pw.cu_seqlens)
+    psrc = torch.tensor([-1], dtype=torch.int32, device="cuda")
+    pdst = torch.tensor([1], dtype=torch.int32, device="cuda")
+    ws = None
+    for _ in range(2):
+        ws = gdn.gdn_prefill_chunked(ppool, pq, pk, pv, pg, pb, po, pcu, pw.cu_seqlens, psrc, pdst, workspace=ws)
+    torch.cuda.synchronize()
+    ppool.close()
     print(json.dumps({"decode_launches": launches,
                       "decode_algorithmic_bytes_per_launch": wl.B * decode_bytes_per_request(wl.HK, wl.HV, wl.dk, wl.dv, 2),
                       "copy_bytes_each_way": n * 4,
@@ -381,6 +474,7 @@ def main():
         run_counters()
         return
     cpu = None if args.no_cpu_baseline else cpu_baseline(decode_bytes_per_request(16, 32, 128, 128, 2))
+    cpu_pre = None if (args.no_cpu_baseline or args.no_prefill) else cpu_baseline_prefill()
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -391,6 +485,9 @@ def main():
 
     d = bench_decode(args.steps, args.warmup)
     pre = None if args.no_prefill else bench_prefill()
+    if pre is not None and not args.no_cpu_baseline:
+        pre["cpu_baseline"] = cpu_pre
+    ach = achievable()
     line = {
         "metric": METRIC,
         "value": round(d["value"], 1),
@@ -421,6 +518,7 @@ def main():
         "cold_cache": {"value": round(d["cold_gbs"], 1), "unit": "GB/s", "frac": round(d["cold_gbs"] / HBM_PEAK_GBS, 4),
                        "protocol": "median of 20 single launches, each after a 1 GiB device write"},
         "cpu_baseline": cpu,
+        "achievable": ach,
         "prefill": pre,
     }
     print(json.dumps(line))
