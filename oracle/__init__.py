@@ -19,5 +19,6 @@ from .gdn_oracle import (  # noqa: F401
     chunked_sequence,
     prefill,
     decode_step,
+    verify_step,
     SlotPoolModel,
 )

@@ -252,6 +252,55 @@ def decode_step(pool, src, dst, q, k, v, g, beta, scale, eps):
     return prefill(pool, cu, src, dst, q, k, v, g, beta, scale, eps)
 
 
+def verify_step(pool, src, dst, lens, q, k, v, g, beta, scale, eps):
+    """Speculative-decode verification: K draft tokens per request in order,
+    the state after draft token i stored to its own slot.
+
+    The index indirection the pages describe for speculative decoding (zubnet.ai
+    (Portuguese), "LightSeek TokenSpeed ...", second paragraph: an index table
+    instead of tensor copies) is read here as follows. Request b starts from
+    pool[src[b]] (zero if src[b] < 0) and runs its first lens[b] draft tokens
+    through the rule, token by token; after token i the state goes to
+    dst[b][i] unless that entry is negative. Accepting a draft prefix is then
+    the index write "current slot = dst[b][a]", and a rejected suffix costs
+    nothing to undo. lens[b] == 0 skips the request; lens None means all K.
+
+    pool: [num_slots, HV, dk, dv] float32, never modified. src: [B];
+    dst: [B, K]; q, k: [B, K, HK, dk]; v: [B, K, HV, dv]; g, beta: [B, K, HV].
+    Returns (o [B, K, HV, dv] fp64, NaN for tokens not verified;
+    new_pool float32; states {(b, i): [HV, dk, dv] fp64} for every stored i).
+    Every request reads its source as the pool held it on entry.
+    """
+    pool = np.asarray(pool, np.float32)
+    src = np.asarray(src, np.int64)
+    dst = np.asarray(dst, np.int64)
+    B, K = dst.shape
+    lens = np.full(B, K, np.int64) if lens is None else np.asarray(lens, np.int64)
+    HV, dk, dv = pool.shape[1:]
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    g = np.asarray(g, np.float64)
+    beta = np.asarray(beta, np.float64)
+    hmap = _head_map(q.shape[2], HV)
+    o = np.full((B, K, HV, dv), np.nan)
+    new_pool = pool.copy()
+    states = {}
+    for b in range(B):
+        n = int(lens[b])
+        if n <= 0:
+            continue
+        H0 = pool[src[b]].astype(np.float64) if src[b] >= 0 else np.zeros((HV, dk, dv))
+        S = np.transpose(H0, (0, 2, 1)).copy()               # S = H^T
+        for i in range(n):
+            S, o[b, i] = gated_delta_token(S, q[b, i, hmap], k[b, i, hmap], v[b, i], g[b, i], beta[b, i], scale, eps)
+            if dst[b, i] >= 0:
+                H = np.transpose(S, (0, 2, 1)).copy()
+                states[(b, i)] = H
+                new_pool[dst[b, i]] = H.astype(np.float32)
+    return o, new_pool, states
+
+
 # ---------------------------------------------------------------------------
 # slot bookkeeping model
 # ---------------------------------------------------------------------------
