@@ -44,6 +44,14 @@ def decode_bytes_per_request(HK, HV, dk, dv, elem):
     return 2 * HV * dk * dv * 4 + 2 * HK * dk * elem + 2 * HV * dv * elem + 8 * HV + 8
 
 
+def verify_bytes_per_request(K, HK, HV, dk, dv, elem):
+    """Algorithmic HBM bytes of verifying K draft tokens of one request with
+    every draft state stored: the source tile read once, K tiles written, and
+    per token q and k, v and o, g and beta; plus the source and K destination
+    indices."""
+    return HV * dk * dv * 4 * (1 + K) + K * (2 * HK * dk * elem + 2 * HV * dv * elem + 8 * HV) + 4 * (1 + K)
+
+
 def prefill_flops_per_token(HV, dk, dv, C=64, G=2):
     """Algorithmic MFMA flops per token of the chunk form (full chunks): W, U',
     U, inter-chunk output, intra-chunk output, state advance, shared Grams."""
@@ -267,6 +275,50 @@ def bench_prefill(reps=20, warmup=3):
     }
 
 
+def bench_verify(reps=50, warmup=5):
+    """Speculative-decode verification: 64 requests x 4 draft tokens at the
+    16/32-head 128 x 128 bf16 shape, every draft state stored (one launch).
+    Launches are idempotent (sources are only read), so `reps` of them run
+    back to back between two events."""
+    import torch
+    from hybrid_linear_attention_02_amd import gdn
+    from hybrid_linear_attention_02_amd.workloads import spec_verify
+
+    wl = spec_verify()
+    B, K = wl.B, wl.K
+    tk = wl.tokens
+    shp = lambda x: np.ascontiguousarray(x.reshape((B, K) + x.shape[1:]))
+    bf = lambda x: torch.from_numpy(shp(x).view(np.int16)).view(torch.bfloat16).cuda()
+    dv_ = lambda x: torch.from_numpy(shp(x)).cuda()
+    q, k, v, g, b = bf(tk.q), bf(tk.k), bf(tk.v), dv_(tk.g), dv_(tk.beta)
+    storage = torch.from_numpy(wl.pool).cuda()
+    pool = gdn.gdn_state_pool_create(wl.num_slots, wl.HV, wl.dk, wl.dv, storage=storage)
+    src = torch.tensor(wl.src, dtype=torch.int32, device="cuda")
+    free = np.setdiff1d(np.arange(wl.num_slots), wl.src)[:B * K]
+    dst = torch.tensor(free.reshape(B, K), dtype=torch.int32, device="cuda")
+    o = torch.empty_like(v)
+    call = lambda: gdn.gdn_decode_verify(pool, q, k, v, g, b, o, src, dst)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    per_req = verify_bytes_per_request(K, wl.HK, wl.HV, wl.dk, wl.dv, 2)
+    gbs = B * per_req / t / 1e9
+    pool.close()
+    return {"workload": "spec_verify_bf16_b64_k4_hk16_hv32_128x128", "value": B * K / t, "unit": "draft tok/s",
+            "us_per_launch": t * 1e6, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "bytes_per_launch": B * per_req,
+            "vs_decode_steps": "one launch reads each source tile once for 4 tokens; 4 decode steps would move "
+                               f"{4 * B * decode_bytes_per_request(wl.HK, wl.HV, wl.dk, wl.dv, 2) / 1e6:.0f} MB "
+                               f"against {B * per_req / 1e6:.0f} MB"}
+
+
 def _oracle_worker(args):
     os.environ["OMP_NUM_THREADS"] = "1"
     (pool_part, src, dst, steps_part, scale, repeats) = args
@@ -487,6 +539,7 @@ def main():
     pre = None if args.no_prefill else bench_prefill()
     if pre is not None and not args.no_cpu_baseline:
         pre["cpu_baseline"] = cpu_pre
+    ver = bench_verify()
     ach = achievable()
     line = {
         "metric": METRIC,
@@ -519,6 +572,7 @@ def main():
                        "protocol": "median of 20 single launches, each after a 1 GiB device write"},
         "cpu_baseline": cpu,
         "achievable": ach,
+        "verify": ver,
         "prefill": pre,
     }
     print(json.dumps(line))

@@ -52,6 +52,35 @@ extern "C" int gdn_decode_step(const gdn_pool* pool, const gdn_decode_args* a, v
     return gdn::launch_decode(pool, a, stream);
 }
 
+extern "C" int gdn_decode_verify(const gdn_pool* pool, const gdn_verify_args* a, void* stream) {
+    const char* fn = "gdn_decode_verify";
+    if (pool == nullptr || a == nullptr) return fail(GDN_E_INVALID, "gdn_decode_verify: NULL pool or args");
+    if (a->batch < 0) return fail(GDN_E_INVALID, "gdn_decode_verify: batch must be >= 0");
+    if (a->num_draft < 1 || a->num_draft > gdn::kMaxDraft)
+        return fail(GDN_E_INVALID, "gdn_decode_verify: num_draft must be in [1, " + std::to_string(gdn::kMaxDraft) + "]");
+    int st = check_heads(pool, a->num_k_heads, a->num_v_heads, a->dk, a->dv, fn);
+    if (st != GDN_OK) return st;
+    if (a->dtype != GDN_DTYPE_F32 && a->dtype != GDN_DTYPE_BF16)
+        return fail(GDN_E_UNSUPPORTED, "gdn_decode_verify: dtype must be GDN_DTYPE_F32 or GDN_DTYPE_BF16");
+    if (!std::isfinite(a->scale) || !(a->l2_eps >= 0.0f) || !std::isfinite(a->l2_eps))
+        return fail(GDN_E_INVALID, "gdn_decode_verify: scale must be finite and l2_eps finite and >= 0");
+    if (static_cast<int64_t>(a->batch) * a->num_v_heads > INT32_MAX ||
+        static_cast<int64_t>(a->batch) * a->num_draft * a->num_v_heads * std::max(a->dk, a->dv) > INT32_MAX)
+        return fail(GDN_E_INVALID, "gdn_decode_verify: batch too large");
+    if (a->batch == 0) return GDN_OK;
+    const void* ptrs[] = {a->q, a->k, a->v, a->g, a->beta, a->o, a->src_slots, a->dst_slots};
+    for (const void* p : ptrs)
+        if (p == nullptr) return fail(GDN_E_INVALID, "gdn_decode_verify: NULL device pointer");
+    const void* vec[] = {a->q, a->k, a->v, a->o};
+    for (const void* p : vec)
+        if (!aligned(p, 16)) return fail(GDN_E_INVALID, "gdn_decode_verify: q, k, v, o must be 16-byte aligned");
+    const void* word[] = {a->g, a->beta, a->src_slots, a->dst_slots, a->draft_lens, a->err_flag};
+    for (const void* p : word)
+        if (!aligned(p, 4))
+            return fail(GDN_E_INVALID, "gdn_decode_verify: g, beta, slot tables, draft_lens, err_flag must be 4-byte aligned");
+    return gdn::launch_verify(pool, a, stream);
+}
+
 extern "C" int gdn_prefill_workspace_bytes(const gdn_pool* pool, const gdn_prefill_args* a, size_t* bytes) {
     if (bytes == nullptr) return fail(GDN_E_INVALID, "gdn_prefill_workspace_bytes: bytes is NULL");
     gdn::PrefillPlan plan;

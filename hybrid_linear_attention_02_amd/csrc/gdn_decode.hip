@@ -51,6 +51,8 @@ struct DecodeParams {
     int32_t num_slots;
     float scale;
     float eps;
+    int32_t ndraft;           // verify: draft tokens per request (K); decode: 1
+    const int32_t* lens;      // verify: [B] draft lengths or null (all K)
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
@@ -114,47 +116,37 @@ struct DecodeShape {
     static_assert(NT % 64 == 0 && 64 % CG == 0 && DK % RG == 0, "unsupported tile shape");
 };
 
+// LDS scratch of one (request, head) workgroup.
+template <int DK, int DV>
+struct TokenScratch {
+    float k[DK];
+    float q[DK];
+    f4 red[DecodeShape<DK, DV>::NW][DecodeShape<DK, DV>::CG][2];
+};
+
+// One token of the rule on the tile slice this thread holds in registers (st):
+// normalise q and k (key head rows at qk_off), reduce H^T k^ and H^T q~ over
+// dk, write the token's output (row gh of o, v, g, beta) and leave the new tile
+// in st. When `out` (a (slot, head) tile) is given, each new row is also
+// stored as soon as it is formed, so the stores start while the rest of the
+// rows are still being read from LDS. `after_token` must be set when the
+// scratch was used by a previous token of the same workgroup (its last
+// readers are then waited for).
 template <int DK, int DV, typename T>
-__global__ void __launch_bounds__(decode_threads(DK, DV)) gdn_decode_kernel(DecodeParams p) {
+__device__ __forceinline__ void token_update(const DecodeParams& p, size_t qk_off, size_t gh,
+                                             f4 (&st)[DecodeShape<DK, DV>::RPT], TokenScratch<DK, DV>& sm,
+                                             bool after_token, f4* out) {
     using Sh = DecodeShape<DK, DV>;
     constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NW = Sh::NW;
     constexpr int KPL = (DK + 63) / 64;   // q/k elements per lane
-
-    __shared__ float s_k[DK];
-    __shared__ float s_q[DK];
-    __shared__ f4 s_red[NW][CG][2];
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int cg = tid % CG;
     const int rg = tid / CG;
-    const int b = blockIdx.x / p.hv;
-    const int h = blockIdx.x - b * p.hv;
 
-    const int d = p.dst[b];
-    if (d < 0) return;                       // padding row
-    const int s = p.src[b];
-    if (d >= p.num_slots || s >= p.num_slots) {
-        if (tid == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
-        return;
-    }
-
-    // 1. Issue the whole source tile first; the rest overlaps its latency.
-    f4 st[RPT];
-    if (s >= 0) {
-        const f4* in = reinterpret_cast<const f4*>(p.pool + (static_cast<size_t>(s) * p.hv + h) * (DK * DV));
-#pragma unroll
-        for (int m = 0; m < RPT; ++m) st[m] = __builtin_nontemporal_load(in + (rg + RG * m) * CG + cg);
-    } else {
-#pragma unroll
-        for (int m = 0; m < RPT; ++m) st[m] = f4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    // 2. L2-normalise k and q of key head h / group (every wave computes the
-    //    sums redundantly; wave 0 publishes the normalised vectors).
-    const int j = h / p.group;
-    const size_t qk_off = (static_cast<size_t>(b) * p.hk + j) * DK;
+    // L2-normalise k and q (every wave computes the sums redundantly; wave 0
+    // publishes the normalised vectors)
     float kx[KPL], qx[KPL];
     float sk = 0.f, sq = 0.f, skq = 0.f;
 #pragma unroll
@@ -175,33 +167,33 @@ __global__ void __launch_bounds__(decode_threads(DK, DV)) gdn_decode_kernel(Deco
     const float rk = 1.0f / sqrtf(sk + p.eps);
     const float rq = p.scale / sqrtf(sq + p.eps);
     const float kq = skq * rk * rq;          // k^ . q~
+    const float eg = expf(p.g[gh]);
+    const float bt = p.beta[gh];
+    const f4 vv = Elem<T>::load4(p.v, gh * DV + 4 * cg);
+    if (after_token) __syncthreads();        // the previous token's readers of sm.k are done
     if (wave == 0) {
 #pragma unroll
         for (int e = 0; e < KPL; ++e) {
             const int i = lane + 64 * e;
             if (i < DK) {
-                s_k[i] = kx[e] * rk;
-                s_q[i] = qx[e] * rq;
+                sm.k[i] = kx[e] * rk;
+                sm.q[i] = qx[e] * rq;
             }
         }
     }
-    const size_t gh = static_cast<size_t>(b) * p.hv + h;
-    const float eg = expf(p.g[gh]);
-    const float bt = p.beta[gh];
-    const f4 vv = Elem<T>::load4(p.v, gh * DV + 4 * cg);
     __syncthreads();
 
-    // 3. Partial H^T k^ and H^T q~ over this thread's rows.
+    // partial H^T k^ and H^T q~ over this thread's rows
     f4 a = f4{0.f, 0.f, 0.f, 0.f};
     f4 c = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int row = rg + RG * m;
-        a += st[m] * s_k[row];
-        c += st[m] * s_q[row];
+        a += st[m] * sm.k[row];
+        c += st[m] * sm.q[row];
     }
-    // 4. Reduce over the row groups: lanes CG apart inside a wave, then the
-    //    waves through LDS, always in the same order (deterministic).
+    // reduce over the row groups: lanes CG apart inside a wave, then the
+    // waves through LDS, always in the same order (deterministic)
 #pragma unroll
     for (int off = CG; off < 64; off <<= 1) {
         a.x += __shfl_xor(a.x, off);
@@ -214,32 +206,137 @@ __global__ void __launch_bounds__(decode_threads(DK, DV)) gdn_decode_kernel(Deco
         c.w += __shfl_xor(c.w, off);
     }
     if (lane < CG) {
-        s_red[wave][lane][0] = a;
-        s_red[wave][lane][1] = c;
+        sm.red[wave][lane][0] = a;
+        sm.red[wave][lane][1] = c;
     }
     __syncthreads();
-    f4 A = s_red[0][cg][0];
-    f4 C = s_red[0][cg][1];
+    f4 A = sm.red[0][cg][0];
+    f4 C = sm.red[0][cg][1];
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
-        A += s_red[w][cg][0];
-        C += s_red[w][cg][1];
+        A += sm.red[w][cg][0];
+        C += sm.red[w][cg][1];
     }
 
-    // 5. Delta correction, output, and the new tile.
+    // delta correction, output, and the new tile
     const f4 u = bt * (vv - eg * A);
     if (rg == 0) Elem<T>::store4(p.o, gh * DV + 4 * cg, eg * C + kq * u);
-    f4* out = reinterpret_cast<f4*>(p.pool + (static_cast<size_t>(d) * p.hv + h) * (DK * DV));
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int row = rg + RG * m;
-        const f4 nv = eg * st[m] + s_k[row] * u;
-        __builtin_nontemporal_store(nv, out + row * CG + cg);
+        st[m] = eg * st[m] + sm.k[row] * u;
+        if (out != nullptr) __builtin_nontemporal_store(st[m], out + row * CG + cg);
     }
 }
 
+// load / store of this thread's slice of a (slot, head) tile, 128-bit
+// non-temporal (a tile is touched once per launch)
+template <int DK, int DV>
+__device__ __forceinline__ void load_tile(const DecodeParams& p, int slot, int h, f4 (&st)[DecodeShape<DK, DV>::RPT]) {
+    using Sh = DecodeShape<DK, DV>;
+    const int cg = threadIdx.x % Sh::CG, rg = threadIdx.x / Sh::CG;
+    if (slot >= 0) {
+        const f4* in = reinterpret_cast<const f4*>(p.pool + (static_cast<size_t>(slot) * p.hv + h) * (DK * DV));
+#pragma unroll
+        for (int m = 0; m < Sh::RPT; ++m) st[m] = __builtin_nontemporal_load(in + (rg + Sh::RG * m) * Sh::CG + cg);
+    } else {
+#pragma unroll
+        for (int m = 0; m < Sh::RPT; ++m) st[m] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// a (slot, head) tile of the pool
+__device__ __forceinline__ f4* tile_ptr(const DecodeParams& p, int slot, int h, int elems) {
+    return reinterpret_cast<f4*>(p.pool + (static_cast<size_t>(slot) * p.hv + h) * elems);
+}
+
 template <int DK, int DV, typename T>
-int launch_shape(const gdn_pool* pool, const gdn_decode_args* a, hipStream_t stream) {
+__global__ void __launch_bounds__(decode_threads(DK, DV)) gdn_decode_kernel(DecodeParams p) {
+    __shared__ TokenScratch<DK, DV> sm;
+    const int b = blockIdx.x / p.hv;
+    const int h = blockIdx.x - b * p.hv;
+
+    const int d = p.dst[b];
+    if (d < 0) return;                       // padding row
+    const int s = p.src[b];
+    if (d >= p.num_slots || s >= p.num_slots) {
+        if (threadIdx.x == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
+        return;
+    }
+    // issue the whole source tile first; the token's small loads overlap its latency
+    f4 st[DecodeShape<DK, DV>::RPT];
+    load_tile<DK, DV>(p, s, h, st);
+    const size_t qk_off = (static_cast<size_t>(b) * p.hk + h / p.group) * DK;
+    token_update<DK, DV, T>(p, qk_off, static_cast<size_t>(b) * p.hv + h, st, sm, false, tile_ptr(p, d, h, DK * DV));
+}
+
+// Speculative-decode verification: draft tokens 0 .. n-1 of request b in
+// order on the tile held in registers; the tile goes to dst[b][i] after token
+// i when that entry is >= 0. The source is read once for all of them.
+template <int DK, int DV, typename T>
+__global__ void __launch_bounds__(decode_threads(DK, DV)) gdn_verify_kernel(DecodeParams p) {
+    __shared__ TokenScratch<DK, DV> sm;
+    const int b = blockIdx.x / p.hv;
+    const int h = blockIdx.x - b * p.hv;
+    const int K = p.ndraft;
+    const int n = p.lens != nullptr ? p.lens[b] : K;
+    if (n == 0) return;
+    if (n < 0 || n > K) {
+        if (threadIdx.x == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_DRAFT_LEN);
+        return;
+    }
+    const int s = p.src[b];
+    bool bad = s >= p.num_slots;
+    for (int i = 0; i < n; ++i) bad |= p.dst[static_cast<size_t>(b) * K + i] >= p.num_slots;
+    if (bad) {
+        if (threadIdx.x == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
+        return;
+    }
+    f4 st[DecodeShape<DK, DV>::RPT];
+    load_tile<DK, DV>(p, s, h, st);
+    const int j = h / p.group;
+    for (int i = 0; i < n; ++i) {
+        const size_t t = static_cast<size_t>(b) * K + i;      // token row
+        const int d = p.dst[t];
+        token_update<DK, DV, T>(p, (t * p.hk + j) * DK, t * p.hv + h, st, sm, i > 0,
+                                d >= 0 ? tile_ptr(p, d, h, DK * DV) : nullptr);
+    }
+}
+
+template <int DK, int DV, typename T, bool VERIFY>
+int launch_shape(const DecodeParams& p, int batch, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(batch) * static_cast<unsigned>(p.hv));
+    if (VERIFY) hipLaunchKernelGGL((gdn_verify_kernel<DK, DV, T>), grid, dim3(DecodeShape<DK, DV>::NT), 0, stream, p);
+    else hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, T>), grid, dim3(DecodeShape<DK, DV>::NT), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return gdn::fail(GDN_E_HIP, std::string(VERIFY ? "gdn_decode_verify" : "gdn_decode_step") + ": launch failed: " +
+                                        hipGetErrorString(e));
+    return GDN_OK;
+}
+
+template <typename T, bool VERIFY>
+int dispatch_dv(const DecodeParams& p, int batch, int dk, int dv, hipStream_t s) {
+#define GDN_DK_CASE(DK)                                                     \
+    if (dk == DK) {                                                         \
+        switch (dv) {                                                       \
+            case 16: return launch_shape<DK, 16, T, VERIFY>(p, batch, s);   \
+            case 32: return launch_shape<DK, 32, T, VERIFY>(p, batch, s);   \
+            case 64: return launch_shape<DK, 64, T, VERIFY>(p, batch, s);   \
+            case 128: return launch_shape<DK, 128, T, VERIFY>(p, batch, s); \
+            default: break;                                                 \
+        }                                                                   \
+    }
+    GDN_DK_CASE(16)
+    GDN_DK_CASE(32)
+    GDN_DK_CASE(64)
+    GDN_DK_CASE(128)
+#undef GDN_DK_CASE
+    return gdn::fail(GDN_E_UNSUPPORTED, std::string(VERIFY ? "gdn_decode_verify" : "gdn_decode_step") + ": unsupported dk/dv");
+}
+
+template <typename A>
+DecodeParams make_params(const gdn_pool* pool, const A* a) {
     DecodeParams p;
     p.q = a->q;
     p.k = a->k;
@@ -257,31 +354,9 @@ int launch_shape(const gdn_pool* pool, const gdn_decode_args* a, hipStream_t str
     p.num_slots = pool->num_slots;
     p.scale = a->scale;
     p.eps = a->l2_eps;
-    const dim3 grid(static_cast<unsigned>(a->batch) * static_cast<unsigned>(a->num_v_heads));
-    hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, T>), grid, dim3(DecodeShape<DK, DV>::NT), 0, stream, p);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return gdn::fail(GDN_E_HIP, std::string("gdn_decode_step: launch failed: ") + hipGetErrorString(e));
-    return GDN_OK;
-}
-
-template <typename T>
-int dispatch_dv(const gdn_pool* pool, const gdn_decode_args* a, hipStream_t s) {
-#define GDN_DK_CASE(DK)                                               \
-    if (a->dk == DK) {                                                \
-        switch (a->dv) {                                              \
-            case 16: return launch_shape<DK, 16, T>(pool, a, s);     \
-            case 32: return launch_shape<DK, 32, T>(pool, a, s);     \
-            case 64: return launch_shape<DK, 64, T>(pool, a, s);     \
-            case 128: return launch_shape<DK, 128, T>(pool, a, s);   \
-            default: break;                                           \
-        }                                                             \
-    }
-    GDN_DK_CASE(16)
-    GDN_DK_CASE(32)
-    GDN_DK_CASE(64)
-    GDN_DK_CASE(128)
-#undef GDN_DK_CASE
-    return gdn::fail(GDN_E_UNSUPPORTED, "gdn_decode_step: unsupported dk/dv");
+    p.ndraft = 1;
+    p.lens = nullptr;
+    return p;
 }
 
 }  // namespace
@@ -290,8 +365,18 @@ namespace gdn {
 
 int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (a->dtype == GDN_DTYPE_F32) return dispatch_dv<float>(pool, a, s);
-    return dispatch_dv<uint16_t>(pool, a, s);
+    const DecodeParams p = make_params(pool, a);
+    if (a->dtype == GDN_DTYPE_F32) return dispatch_dv<float, false>(p, a->batch, a->dk, a->dv, s);
+    return dispatch_dv<uint16_t, false>(p, a->batch, a->dk, a->dv, s);
+}
+
+int launch_verify(const gdn_pool* pool, const gdn_verify_args* a, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DecodeParams p = make_params(pool, a);
+    p.ndraft = a->num_draft;
+    p.lens = a->draft_lens;
+    if (a->dtype == GDN_DTYPE_F32) return dispatch_dv<float, true>(p, a->batch, a->dk, a->dv, s);
+    return dispatch_dv<uint16_t, true>(p, a->batch, a->dk, a->dv, s);
 }
 
 }  // namespace gdn

@@ -27,6 +27,8 @@ int fail(int code, const std::string& msg);
 // Kernel launchers (defined in the .hip files). They assume validated
 // arguments and return GDN_OK or GDN_E_HIP / GDN_E_UNSUPPORTED.
 int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream);
+constexpr int kMaxDraft = 64;     // draft tokens per request in one verify launch
+int launch_verify(const gdn_pool* pool, const gdn_verify_args* a, void* stream);
 
 // Sequence split of long prefills. A sequence of more than seg_len chunks is
 // cut into segments of seg_len chunks; each segment's local end state E and

@@ -29,6 +29,7 @@ GDN_DTYPE_F32 = 0
 GDN_DTYPE_BF16 = 1
 
 GDN_ERRFLAG_SLOT_RANGE = 1
+GDN_ERRFLAG_DRAFT_LEN = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 
@@ -37,7 +38,7 @@ EXPORTED = (
     "gdn_state_pool_retain", "gdn_state_pool_release", "gdn_state_pool_cow",
     "gdn_state_pool_validate", "gdn_state_pool_refcount", "gdn_state_pool_num_free",
     "gdn_state_pool_capacity", "gdn_decode_step", "gdn_prefill_workspace_bytes",
-    "gdn_prefill_chunked", "gdn_last_error",
+    "gdn_decode_verify", "gdn_prefill_chunked", "gdn_last_error",
 )
 
 
@@ -53,6 +54,16 @@ class DecodeArgs(ctypes.Structure):
         ("dk", c_int32), ("dv", c_int32), ("dtype", c_int32),
         ("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("g", c_void_p), ("beta", c_void_p),
         ("o", c_void_p), ("src_slots", c_void_p), ("dst_slots", c_void_p),
+        ("scale", c_float), ("l2_eps", c_float), ("err_flag", c_void_p),
+    ]
+
+
+class VerifyArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", c_int32), ("num_draft", c_int32), ("num_k_heads", c_int32), ("num_v_heads", c_int32),
+        ("dk", c_int32), ("dv", c_int32), ("dtype", c_int32),
+        ("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("g", c_void_p), ("beta", c_void_p),
+        ("o", c_void_p), ("src_slots", c_void_p), ("dst_slots", c_void_p), ("draft_lens", c_void_p),
         ("scale", c_float), ("l2_eps", c_float), ("err_flag", c_void_p),
     ]
 
@@ -95,6 +106,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_state_pool_num_free": ([P, POINTER(c_int32)], c_int32),
         "gdn_state_pool_capacity": ([P, POINTER(c_int32)], c_int32),
         "gdn_decode_step": ([P, POINTER(DecodeArgs), P], c_int32),
+        "gdn_decode_verify": ([P, POINTER(VerifyArgs), P], c_int32),
         "gdn_prefill_workspace_bytes": ([P, POINTER(PrefillArgs), POINTER(c_size_t)], c_int32),
         "gdn_prefill_chunked": ([P, POINTER(PrefillArgs), P, c_size_t, P], c_int32),
         "gdn_last_error": ([], c_char_p),
@@ -293,6 +305,41 @@ def gdn_decode_step(pool: StatePool, q, k, v, g, beta, o, src_slots, dst_slots, 
     a.l2_eps = float(l2_eps)
     a.err_flag = _dev(err_flag, "err_flag", torch.int32)
     _check(load_library().gdn_decode_step(c_void_p(pool.handle), byref(a), _stream(stream)))
+
+
+def gdn_decode_verify(pool: StatePool, q, k, v, g, beta, o, src_slots, dst_slots, *, draft_lens=None,
+                      scale=None, l2_eps: float = 1e-6, err_flag=None, stream=None) -> None:
+    """Speculative-decode verification, K draft tokens per request in one
+    launch. q, k: [B, K, HK, dk]; v, o: [B, K, HV, dv] (all float32 or all
+    bfloat16); g, beta: float32 [B, K, HV]; src: int32 device [B]; dst: int32
+    device [B, K] (state after draft token i -> dst[b, i], < 0 = not stored);
+    draft_lens: optional int32 device [B] (tokens verified per request).
+    Enqueued on ``stream`` (default: the current stream)."""
+    import torch
+    B, K, HK, dk = q.shape
+    HV, dv = v.shape[2], v.shape[3]
+    dt = _dtype_code(q)
+    for t, n in ((k, "k"), (v, "v"), (o, "o")):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{n} must have q's dtype")
+    if tuple(k.shape) != (B, K, HK, dk) or tuple(v.shape) != (B, K, HV, dv) or tuple(o.shape) != (B, K, HV, dv):
+        raise ValueError("q/k/v/o shapes disagree")
+    if tuple(g.shape) != (B, K, HV) or tuple(beta.shape) != (B, K, HV):
+        raise ValueError("g and beta must be [B, K, HV]")
+    if src_slots.numel() != B or tuple(dst_slots.shape) != (B, K):
+        raise ValueError("src must have B entries and dst shape [B, K]")
+    if draft_lens is not None and draft_lens.numel() != B:
+        raise ValueError("draft_lens must have B entries")
+    a = VerifyArgs()
+    a.batch, a.num_draft, a.num_k_heads, a.num_v_heads, a.dk, a.dv, a.dtype = B, K, HK, HV, dk, dv, dt
+    a.q, a.k, a.v, a.o = _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o")
+    a.g, a.beta = _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
+    a.src_slots, a.dst_slots = _dev(src_slots, "src_slots", torch.int32), _dev(dst_slots, "dst_slots", torch.int32)
+    a.draft_lens = _dev(draft_lens, "draft_lens", torch.int32)
+    a.scale = float(dk ** -0.5 if scale is None else scale)
+    a.l2_eps = float(l2_eps)
+    a.err_flag = _dev(err_flag, "err_flag", torch.int32)
+    _check(load_library().gdn_decode_verify(c_void_p(pool.handle), byref(a), _stream(stream)))
 
 
 def _prefill_args(pool, q, k, v, g, beta, o, cu_seqlens, cu_seqlens_host, src_slots, dst_slots,

@@ -110,6 +110,35 @@ class PrefillWorkload:
     chunk: int = 64
 
 
+@dataclass
+class VerifyWorkload:
+    """K draft tokens per request for speculative-decode verification; token
+    (b, i) is row b * K + i of `tokens`."""
+    name: str
+    B: int
+    K: int
+    HK: int
+    HV: int
+    dk: int
+    dv: int
+    dtype: str
+    num_slots: int
+    pool: np.ndarray                 # [num_slots, HV, dk, dv] float32
+    src: np.ndarray                  # [B] int32
+    tokens: Tokens = None            # T = B * K
+
+
+def verify_workload(name, *, seed, B, K, HK, HV, dk, dv, dtype, num_slots, pool_sigma,
+                    src=None, g_range=(0.01, 0.5), beta_mode="sigmoid") -> VerifyWorkload:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pool = (rng.standard_normal((num_slots, HV, dk, dv), dtype=np.float32) * np.float32(pool_sigma)).astype(np.float32)
+    if src is None:
+        src = rng.permutation(num_slots)[:B]
+    src = np.asarray(src, np.int32)
+    toks = draw_tokens(rng, B * K, HK, HV, dk, dv, dtype, g_range=g_range, beta_mode=beta_mode)
+    return VerifyWorkload(name, B, K, HK, HV, dk, dv, dtype, num_slots, pool, src, toks)
+
+
 def decode_workload(name, *, seed, B, HK, HV, dk, dv, dtype, num_slots, pool_sigma,
                     steps, src=None, g_range=(0.01, 0.5), beta_mode="sigmoid") -> DecodeWorkload:
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -187,3 +216,12 @@ def long_packed_prefill(first=50_000, n_short=16, lo=1024, hi=16384, seed=4) -> 
     lengths = [first] + [int(x) for x in rng.integers(lo, hi, size=n_short, endpoint=True)]
     return prefill_workload("long_packed_prefill_bf16_h32_128x128", seed=seed + 100, lengths=lengths,
                             HK=16, HV=32, dk=128, dv=128, dtype=BF16, num_slots=len(lengths) + 1)
+
+
+def spec_verify(B=64, K=4) -> VerifyWorkload:
+    """Speculative-decode verification at the batched-decode head shape: 64
+    requests, 4 draft tokens each, 16/32 heads, 128 x 128 bf16, seed 5. The
+    pool has room for the sources and one destination per draft position
+    (B (K + 1) slots, ~N(0, 0.05)); sources are a random permutation."""
+    return verify_workload("spec_verify_bf16_b64_k4_h32_128x128", seed=5, B=B, K=K, HK=16, HV=32, dk=128, dv=128,
+                           dtype=BF16, num_slots=B * (K + 1), pool_sigma=0.05)

@@ -67,6 +67,7 @@ extern "C" {
 
 /* bits of the optional device error flag (int32, set by kernels, never cleared) */
 #define GDN_ERRFLAG_SLOT_RANGE 1   /* a src/dst slot index >= num_slots was skipped */
+#define GDN_ERRFLAG_DRAFT_LEN  2   /* a draft length outside [0, num_draft] was skipped (verify) */
 
 typedef struct gdn_pool gdn_pool;   /* opaque host-side handle */
 
@@ -147,6 +148,50 @@ typedef struct gdn_decode_args {
  * skipped in the kernel and flagged in err_flag. Asynchronous on `stream`,
  * no allocation, no host synchronisation, graph-capturable. */
 int gdn_decode_step(const gdn_pool* pool, const gdn_decode_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* speculative-decode verification: K draft tokens per request               */
+/* ------------------------------------------------------------------------ */
+
+/* zubnet.ai (Portuguese), "LightSeek TokenSpeed ...", second paragraph: during
+ * speculative decoding the engine addresses state through an index table
+ * instead of copying tensors. Here one launch runs each request's draft
+ * tokens through the rule in order and stores the state after draft token i
+ * to its own slot, so accepting a draft prefix is the index write
+ * "current slot = dst[b][a]" and a rejected suffix needs no undo. */
+typedef struct gdn_verify_args {
+    int32_t batch;          /* B >= 0 requests */
+    int32_t num_draft;      /* K, 1 <= K <= 64 draft tokens per request */
+    int32_t num_k_heads;    /* HK, divides num_v_heads */
+    int32_t num_v_heads;    /* HV, must equal the pool's */
+    int32_t dk, dv;         /* must equal the pool's */
+    int32_t dtype;          /* GDN_DTYPE_F32 or GDN_DTYPE_BF16: q, k, v, o */
+    const void* q;          /* [B][K][HK][dk] device */
+    const void* k;          /* [B][K][HK][dk] device */
+    const void* v;          /* [B][K][HV][dv] device */
+    const float* g;         /* [B][K][HV] device, log-decay */
+    const float* beta;      /* [B][K][HV] device */
+    void* o;                /* [B][K][HV][dv] device, written for verified tokens */
+    const int32_t* src_slots;  /* [B] device: < 0 = zero initial state */
+    const int32_t* dst_slots;  /* [B][K] device: state after draft token i -> dst[b*K+i]; < 0 = not stored */
+    const int32_t* draft_lens; /* [B] device, or NULL for all K: request b verifies its first
+                                  draft_lens[b] tokens (0 = request skipped) */
+    float scale;            /* applied to q after normalisation (usually dk^-1/2) */
+    float l2_eps;
+    int32_t* err_flag;      /* optional device int32; GDN_ERRFLAG_* bits OR-ed in */
+} gdn_verify_args;
+
+/* For every request, read pool[src[b]] once, apply its verified draft tokens
+ * one after another (each exactly as gdn_decode_step would), write the output
+ * of every verified token and store the state after token i to dst[b][i]
+ * when that entry is >= 0. Tokens past draft_lens[b] leave outputs and slots
+ * untouched. Slot tables follow gdn_state_pool_validate applied to the flat
+ * table of pairs (src[b], dst[b][i]): destinations distinct, none equal to
+ * another request's source; dst[b][i] == src[b] (in place) is allowed. A
+ * request with an out-of-range slot or draft length is skipped and flagged in
+ * err_flag. Asynchronous on `stream`, no allocation, no host synchronisation,
+ * graph-capturable. */
+int gdn_decode_verify(const gdn_pool* pool, const gdn_verify_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* chunked prefill: variable-length sequences packed by cu_seqlens           */

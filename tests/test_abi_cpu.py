@@ -192,6 +192,53 @@ def test_decode_empty_batch_is_a_no_op(lib):
     lib.gdn_state_pool_destroy(h)
 
 
+def _verify_args(addr, **kw):
+    a = gdn.VerifyArgs()
+    a.batch, a.num_draft, a.num_k_heads, a.num_v_heads, a.dk, a.dv = 4, 3, 1, 2, 16, 16
+    a.dtype = gdn.GDN_DTYPE_BF16
+    for f in ("q", "k", "v", "g", "beta", "o", "src_slots", "dst_slots"):
+        setattr(a, f, addr)
+    a.draft_lens, a.scale, a.l2_eps, a.err_flag = None, 0.25, 1e-6, None
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(batch=-1), gdn.GDN_E_INVALID),
+    (dict(num_draft=0), gdn.GDN_E_INVALID),
+    (dict(num_draft=65), gdn.GDN_E_INVALID),
+    (dict(num_k_heads=3, num_v_heads=2), gdn.GDN_E_INVALID),
+    (dict(dv=32), gdn.GDN_E_INVALID),                          # pool has dv = 16
+    (dict(dtype=5), gdn.GDN_E_UNSUPPORTED),
+    (dict(o=None), gdn.GDN_E_INVALID),
+    (dict(src_slots=None), gdn.GDN_E_INVALID),
+    (dict(l2_eps=float("nan")), gdn.GDN_E_INVALID),
+    ("misaligned_q", gdn.GDN_E_INVALID),
+    ("misaligned_lens", gdn.GDN_E_INVALID),
+])
+def test_verify_argument_errors(lib, change, code):
+    buf, h = _make_pool(lib)
+    _, addr = _fake_storage()
+    if change == "misaligned_q":
+        a = _verify_args(addr, q=addr + 4)
+    elif change == "misaligned_lens":
+        a = _verify_args(addr, draft_lens=addr + 2)
+    else:
+        a = _verify_args(addr, **change)
+    assert lib.gdn_decode_verify(h, byref(a), None) == code
+    assert len(lib.gdn_last_error()) > 0
+    lib.gdn_state_pool_destroy(h)
+
+
+def test_verify_empty_batch_is_a_no_op(lib):
+    buf, h = _make_pool(lib)
+    a = _verify_args(None, batch=0)
+    assert lib.gdn_decode_verify(h, byref(a), None) == gdn.GDN_OK
+    assert lib.gdn_decode_verify(None, byref(a), None) == gdn.GDN_E_INVALID
+    lib.gdn_state_pool_destroy(h)
+
+
 def _prefill_args(addr, cu_host, **kw):
     a = gdn.PrefillArgs()
     a.num_seqs = len(cu_host) - 1
