@@ -20,5 +20,7 @@ from .gdn_oracle import (  # noqa: F401
     prefill,
     decode_step,
     verify_step,
+    state_pack,
+    state_unpack,
     SlotPoolModel,
 )

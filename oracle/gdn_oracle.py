@@ -301,6 +301,31 @@ def verify_step(pool, src, dst, lens, q, k, v, g, beta, scale, eps):
     return o, new_pool, states
 
 
+def state_pack(pool, slots):
+    """Gather slot tiles for a state hand-over (24-ai.news, English, section
+    "What are the key optimizations behind the record?", item "Prefill-Decode
+    disaggregation": the two phases hand their state over). Entry i is the
+    tile of slots[i], or a zero state when slots[i] < 0. Returns float32
+    [n, HV, dk, dv]; the pool is not modified."""
+    pool = np.asarray(pool, np.float32)
+    slots = np.asarray(slots, np.int64)
+    out = np.zeros((len(slots),) + pool.shape[1:], np.float32)
+    for i, s in enumerate(slots):
+        if s >= 0:
+            out[i] = pool[s]
+    return out
+
+
+def state_unpack(pool, slots, buffer):
+    """Scatter a packed buffer back into slots: pool[slots[i]] <- buffer[i],
+    skipping negative entries. Returns the new pool (float32 copy)."""
+    new_pool = np.asarray(pool, np.float32).copy()
+    for i, s in enumerate(np.asarray(slots, np.int64)):
+        if s >= 0:
+            new_pool[s] = np.asarray(buffer[i], np.float32)
+    return new_pool
+
+
 # ---------------------------------------------------------------------------
 # slot bookkeeping model
 # ---------------------------------------------------------------------------

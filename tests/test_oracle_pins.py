@@ -25,6 +25,8 @@ from oracle import (
     l2_normalize,
     prefill,
     recurrent_sequence,
+    state_pack,
+    state_unpack,
     verify_step,
 )
 from hybrid_linear_attention_02_amd.workloads import f32_to_bf16_bits
@@ -446,6 +448,35 @@ def test_verify_in_place_first_position_reads_original():
     o_r, H_r = recurrent_sequence(pool[7].astype(np.float64), q[0], k[0], v[0], g[0], b[0], 0.5, 1e-6)
     assert _nrm_err(o[0], o_r) < 1e-13
     assert _nrm_err(states[(0, 2)], H_r) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# state hand-over (pack / unpack)
+# ---------------------------------------------------------------------------
+
+def test_pack_unpack_round_trip_and_edge_entries():
+    rng = np.random.default_rng(41)
+    pool = rng.standard_normal((9, 2, 3, 5)).astype(np.float32)
+    buf = state_pack(pool, [4, -1, 0, 4])
+    np.testing.assert_array_equal(buf[0], pool[4])
+    np.testing.assert_array_equal(buf[2], pool[0])
+    np.testing.assert_array_equal(buf[3], pool[4])                 # a slot may be packed twice
+    assert not buf[1].any()                                        # negative slot: zero state
+    # into another pool: the moved tiles are the originals, bit for bit
+    other = rng.standard_normal((6, 2, 3, 5)).astype(np.float32)
+    new = state_unpack(other, [5, 2, -1, 0], buf)
+    np.testing.assert_array_equal(new[5], pool[4])
+    np.testing.assert_array_equal(new[2], np.zeros((2, 3, 5), np.float32))
+    np.testing.assert_array_equal(new[0], pool[4])
+    np.testing.assert_array_equal(new[np.r_[1, 3, 4]], other[np.r_[1, 3, 4]])   # untouched slots
+    # a decode continued from the moved state equals one continued from the original
+    q = rng.standard_normal((1, 1, 3)); k = rng.standard_normal((1, 1, 3))
+    v = rng.standard_normal((1, 2, 5)); g = -rng.uniform(0, 1, (1, 2)); b = rng.uniform(0, 1, (1, 2))
+    o1, p1, f1 = decode_step(pool, [0], [7], q, k, v, g, b, 0.5, 1e-6)
+    o3, p3, f3 = decode_step(state_unpack(np.zeros((3, 2, 3, 5), np.float32), [1], state_pack(pool, [0])),
+                             [1], [2], q, k, v, g, b, 0.5, 1e-6)
+    np.testing.assert_array_equal(o1, o3)
+    np.testing.assert_array_equal(p1[7], p3[2])
 
 
 # ---------------------------------------------------------------------------
