@@ -319,6 +319,41 @@ def bench_verify(reps=50, warmup=5):
                                f"against {B * per_req / 1e6:.0f} MB"}
 
 
+def bench_transfer(reps=20):
+    """State hand-over: pack the 64 batched-decode requests' slots (all 32
+    heads, 128 x 128 fp32: 134 MB) into one buffer, then unpack it into other
+    slots; GB/s counts bytes read plus bytes written."""
+    import torch
+    from hybrid_linear_attention_02_amd import gdn
+    from hybrid_linear_attention_02_amd.workloads import batched_decode
+
+    wl = batched_decode(steps=1)
+    storage = torch.from_numpy(wl.pool).cuda()
+    pool = gdn.gdn_state_pool_create(wl.num_slots, wl.HV, wl.dk, wl.dv, storage=storage)
+    src = torch.tensor(wl.src, dtype=torch.int32, device="cuda")
+    dst = torch.tensor(np.setdiff1d(np.arange(wl.num_slots), wl.src)[:wl.B], dtype=torch.int32, device="cuda")
+    buf = torch.empty((wl.B, wl.HV, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+    nbytes = buf.numel() * 4
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    tp = timed(lambda: gdn.gdn_state_pool_pack(pool, src, buf))
+    tu = timed(lambda: gdn.gdn_state_pool_unpack(pool, dst, buf))
+    pool.close()
+    return {"workload": "pack/unpack of 64 slots x 32 heads x 128x128 fp32", "bytes_each_way": nbytes,
+            "pack_us": tp * 1e6, "pack_gbs": 2 * nbytes / tp / 1e9,
+            "unpack_us": tu * 1e6, "unpack_gbs": 2 * nbytes / tu / 1e9}
+
+
 def _oracle_worker(args):
     os.environ["OMP_NUM_THREADS"] = "1"
     (pool_part, src, dst, steps_part, scale, repeats) = args
@@ -540,6 +575,7 @@ def main():
     if pre is not None and not args.no_cpu_baseline:
         pre["cpu_baseline"] = cpu_pre
     ver = bench_verify()
+    xfer = bench_transfer()
     ach = achievable()
     line = {
         "metric": METRIC,
@@ -573,6 +609,7 @@ def main():
         "cpu_baseline": cpu,
         "achievable": ach,
         "verify": ver,
+        "transfer": xfer,
         "prefill": pre,
     }
     print(json.dumps(line))

@@ -27,6 +27,29 @@ static int check_heads(const gdn_pool* pool, int32_t hk, int32_t hv, int32_t dk,
     return GDN_OK;
 }
 
+static int transfer(const gdn_pool* pool, bool pack, int32_t n, const int32_t* slots, const float* buffer,
+                    int32_t* err_flag, void* stream) {
+    const std::string fn = pack ? "gdn_state_pool_pack" : "gdn_state_pool_unpack";
+    if (pool == nullptr) return fail(GDN_E_INVALID, fn + ": NULL pool");
+    if (n < 0) return fail(GDN_E_INVALID, fn + ": n must be >= 0");
+    if (static_cast<int64_t>(n) * pool->num_v_heads > INT32_MAX) return fail(GDN_E_INVALID, fn + ": n too large");
+    if (n == 0) return GDN_OK;
+    if (slots == nullptr || buffer == nullptr) return fail(GDN_E_INVALID, fn + ": NULL slot table or buffer");
+    if (!aligned(buffer, 16)) return fail(GDN_E_INVALID, fn + ": buffer must be 16-byte aligned");
+    if (!aligned(slots, 4) || !aligned(err_flag, 4)) return fail(GDN_E_INVALID, fn + ": slots, err_flag must be 4-byte aligned");
+    return gdn::launch_transfer(pool, pack, n, slots, const_cast<float*>(buffer), err_flag, stream);
+}
+
+extern "C" int gdn_state_pool_pack(const gdn_pool* pool, int32_t n, const int32_t* slots, float* buffer,
+                                   int32_t* err_flag, void* stream) {
+    return transfer(pool, true, n, slots, buffer, err_flag, stream);
+}
+
+extern "C" int gdn_state_pool_unpack(const gdn_pool* pool, int32_t n, const int32_t* slots, const float* buffer,
+                                     int32_t* err_flag, void* stream) {
+    return transfer(pool, false, n, slots, buffer, err_flag, stream);
+}
+
 extern "C" int gdn_decode_step(const gdn_pool* pool, const gdn_decode_args* a, void* stream) {
     const char* fn = "gdn_decode_step";
     if (pool == nullptr || a == nullptr) return fail(GDN_E_INVALID, "gdn_decode_step: NULL pool or args");

@@ -29,6 +29,8 @@ int fail(int code, const std::string& msg);
 int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream);
 constexpr int kMaxDraft = 64;     // draft tokens per request in one verify launch
 int launch_verify(const gdn_pool* pool, const gdn_verify_args* a, void* stream);
+int launch_transfer(const gdn_pool* pool, bool pack, int32_t n, const int32_t* slots, float* buffer,
+                    int32_t* err_flag, void* stream);
 
 // Sequence split of long prefills. A sequence of more than seg_len chunks is
 // cut into segments of seg_len chunks; each segment's local end state E and

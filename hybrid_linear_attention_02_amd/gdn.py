@@ -38,7 +38,8 @@ EXPORTED = (
     "gdn_state_pool_retain", "gdn_state_pool_release", "gdn_state_pool_cow",
     "gdn_state_pool_validate", "gdn_state_pool_refcount", "gdn_state_pool_num_free",
     "gdn_state_pool_capacity", "gdn_decode_step", "gdn_prefill_workspace_bytes",
-    "gdn_decode_verify", "gdn_prefill_chunked", "gdn_last_error",
+    "gdn_decode_verify", "gdn_prefill_chunked", "gdn_last_error", "gdn_state_pool_pack",
+    "gdn_state_pool_unpack",
 )
 
 
@@ -105,6 +106,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_state_pool_refcount": ([P, c_int32, POINTER(c_int32)], c_int32),
         "gdn_state_pool_num_free": ([P, POINTER(c_int32)], c_int32),
         "gdn_state_pool_capacity": ([P, POINTER(c_int32)], c_int32),
+        "gdn_state_pool_pack": ([P, c_int32, P, P, P, P], c_int32),
+        "gdn_state_pool_unpack": ([P, c_int32, P, P, P, P], c_int32),
         "gdn_decode_step": ([P, POINTER(DecodeArgs), P], c_int32),
         "gdn_decode_verify": ([P, POINTER(VerifyArgs), P], c_int32),
         "gdn_prefill_workspace_bytes": ([P, POINTER(PrefillArgs), POINTER(c_size_t)], c_int32),
@@ -305,6 +308,30 @@ def gdn_decode_step(pool: StatePool, q, k, v, g, beta, o, src_slots, dst_slots, 
     a.l2_eps = float(l2_eps)
     a.err_flag = _dev(err_flag, "err_flag", torch.int32)
     _check(load_library().gdn_decode_step(c_void_p(pool.handle), byref(a), _stream(stream)))
+
+
+def gdn_state_pool_pack(pool: StatePool, slots, buffer, *, err_flag=None, stream=None) -> None:
+    """buffer[i] <- pool tile of slots[i] (zero state for a negative slot).
+    slots: int32 device [n]; buffer: float32 device [n, HV, dk, dv]."""
+    import torch
+    n = slots.numel()
+    if tuple(buffer.shape) != (n, pool.num_v_heads, pool.dk, pool.dv):
+        raise ValueError("buffer must be [n, HV, dk, dv]")
+    _check(load_library().gdn_state_pool_pack(
+        c_void_p(pool.handle), n, _dev(slots, "slots", torch.int32), _dev(buffer, "buffer", torch.float32),
+        _dev(err_flag, "err_flag", torch.int32), _stream(stream)))
+
+
+def gdn_state_pool_unpack(pool: StatePool, slots, buffer, *, err_flag=None, stream=None) -> None:
+    """pool tile of slots[i] <- buffer[i] (negative slots skipped; the others
+    distinct). slots: int32 device [n]; buffer: float32 device [n, HV, dk, dv]."""
+    import torch
+    n = slots.numel()
+    if tuple(buffer.shape) != (n, pool.num_v_heads, pool.dk, pool.dv):
+        raise ValueError("buffer must be [n, HV, dk, dv]")
+    _check(load_library().gdn_state_pool_unpack(
+        c_void_p(pool.handle), n, _dev(slots, "slots", torch.int32), _dev(buffer, "buffer", torch.float32),
+        _dev(err_flag, "err_flag", torch.int32), _stream(stream)))
 
 
 def gdn_decode_verify(pool: StatePool, q, k, v, g, beta, o, src_slots, dst_slots, *, draft_lens=None,

@@ -120,6 +120,30 @@ int gdn_state_pool_num_free(const gdn_pool* pool, int32_t* out);
 int gdn_state_pool_capacity(const gdn_pool* pool, int32_t* out);
 
 /* ------------------------------------------------------------------------ */
+/* state transfer                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* 24-ai.news (English), section "What are the key optimizations behind the
+ * record?", item "Prefill-Decode disaggregation": the context-filling and
+ * token-generation phases run apart and hand their state over. These two calls
+ * are the one-GPU half of that hand-over. pack copies the tiles of n slots into
+ * one contiguous device buffer that a transport can move; unpack writes such a
+ * buffer into slots of a pool with the same head shape (HV, dk, dv).
+ *
+ * slots: [n] device int32. buffer: [n][HV][dk][dv] device float32, 16-byte
+ * aligned. pack: entry i <- pool[slots[i]]; slots[i] < 0 writes a zero state.
+ * unpack: pool[slots[i]] <- entry i; slots[i] < 0 skips the entry; the
+ * non-negative slots must be distinct. A slot >= num_slots skips its entry and
+ * sets GDN_ERRFLAG_SLOT_RANGE in err_flag (optional). Bit-exact copies, no
+ * refcount change (the caller owns the bookkeeping). Asynchronous on `stream`,
+ * no allocation, graph-capturable. Errors: GDN_E_INVALID (n < 0, NULL or
+ * misaligned pointers when n > 0). */
+int gdn_state_pool_pack(const gdn_pool* pool, int32_t n, const int32_t* slots, float* buffer, int32_t* err_flag,
+                        void* stream);
+int gdn_state_pool_unpack(const gdn_pool* pool, int32_t n, const int32_t* slots, const float* buffer,
+                          int32_t* err_flag, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* decode: one token per request                                             */
 /* ------------------------------------------------------------------------ */
 

@@ -239,6 +239,21 @@ def test_verify_empty_batch_is_a_no_op(lib):
     lib.gdn_state_pool_destroy(h)
 
 
+def test_pack_unpack_argument_errors(lib):
+    buf, h = _make_pool(lib)
+    _, addr = _fake_storage()
+    for fn in (lib.gdn_state_pool_pack, lib.gdn_state_pool_unpack):
+        assert fn(h, 0, None, None, None, None) == gdn.GDN_OK                 # nothing to do
+        assert fn(None, 1, c_void_p(addr), c_void_p(addr), None, None) == gdn.GDN_E_INVALID
+        assert fn(h, -1, c_void_p(addr), c_void_p(addr), None, None) == gdn.GDN_E_INVALID
+        assert fn(h, 2, None, c_void_p(addr), None, None) == gdn.GDN_E_INVALID
+        assert fn(h, 2, c_void_p(addr), None, None, None) == gdn.GDN_E_INVALID
+        assert fn(h, 2, c_void_p(addr), c_void_p(addr + 8), None, None) == gdn.GDN_E_INVALID   # buffer alignment
+        assert fn(h, 2, c_void_p(addr + 2), c_void_p(addr), None, None) == gdn.GDN_E_INVALID   # slot table alignment
+        assert len(lib.gdn_last_error()) > 0
+    lib.gdn_state_pool_destroy(h)
+
+
 def _prefill_args(addr, cu_host, **kw):
     a = gdn.PrefillArgs()
     a.num_seqs = len(cu_host) - 1
