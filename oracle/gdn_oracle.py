@@ -196,7 +196,8 @@ def chunked_sequence(H0, q, k, v, g, beta, scale, eps, chunk):
 # slot-addressed prefill and decode over a state pool
 # ---------------------------------------------------------------------------
 
-def prefill(pool, cu_seqlens, src, dst, q, k, v, g, beta, scale, eps, *, chunk=None):
+def prefill(pool, cu_seqlens, src, dst, q, k, v, g, beta, scale, eps, *, chunk=None, ckpt=None,
+            ckpt_states=None):
     """Varlen prefill over a slot pool, token by token (or chunk form if chunk).
 
     pool: [num_slots, HV, dk, dv] float32 tiles (H = S^T); never modified.
@@ -210,6 +211,17 @@ def prefill(pool, cu_seqlens, src, dst, q, k, v, g, beta, scale, eps, *, chunk=N
     Every sequence reads its source tile from the pool as it was on entry, so
     an in-place entry (src == dst) and entries sharing one source all see the
     original bytes; slots that are not destinations keep their bytes.
+
+    Periodic checkpoints (the pages' hybrid prefix caching checkpoints the
+    linear-attention state beside the KV pages -- 24-ai.news (English), section
+    "What are the key optimizations behind the record?", item "Hybrid prefix
+    caching for GDN/Mamba"): ckpt is an optional table over the 64-token
+    chunks of all written sequences in order (sequence n owns
+    ceil(len_n / 64) entries, skipped sequences own theirs too). When
+    ckpt[c] >= 0 the state after chunk c -- after token min(64 (j + 1), len)
+    of its sequence, j the chunk's index in it -- is stored to slot ckpt[c]
+    (after the destinations). If ckpt_states is a dict it receives
+    {c: [HV, dk, dv] fp64} for every stored checkpoint.
     """
     pool = np.asarray(pool, np.float32)
     cu = np.asarray(cu_seqlens, np.int64)
@@ -220,24 +232,40 @@ def prefill(pool, cu_seqlens, src, dst, q, k, v, g, beta, scale, eps, *, chunk=N
     o = np.full((T, HV, dv), np.nan)
     new_pool = pool.copy()
     finals = {}
+    stored = {}
+    c_first = 0                                   # first chunk of sequence n in the ckpt table
     for n in range(len(src)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        nchunks = (b - a + 63) // 64
+        c0, c_first = c_first, c_first + nchunks
         if dst[n] < 0:
             continue
-        a, b = int(cu[n]), int(cu[n + 1])
         if src[n] >= 0:
             H0 = pool[src[n]].astype(np.float64)
         else:
             H0 = np.zeros((HV, dk, dv))
         if b > a:
-            if chunk is None:
-                on, Hn = recurrent_sequence(H0, q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], scale, eps)
+            run = (lambda H, s, e: recurrent_sequence(H, q[s:e], k[s:e], v[s:e], g[s:e], beta[s:e], scale, eps)) \
+                if chunk is None else \
+                (lambda H, s, e: chunked_sequence(H, q[s:e], k[s:e], v[s:e], g[s:e], beta[s:e], scale, eps, chunk))
+            if ckpt is None:
+                on, Hn = run(H0, a, b)
+                o[a:b] = on
             else:
-                on, Hn = chunked_sequence(H0, q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], scale, eps, chunk)
-            o[a:b] = on
+                Hn = H0
+                for j in range(nchunks):
+                    s_, e_ = a + 64 * j, min(a + 64 * (j + 1), b)
+                    o[s_:e_], Hn = run(Hn, s_, e_)
+                    if ckpt[c0 + j] >= 0:
+                        stored[c0 + j] = Hn.copy()
         else:
             Hn = H0.copy()
         finals[n] = Hn
         new_pool[dst[n]] = Hn.astype(np.float32)
+    for c, Hc in stored.items():
+        new_pool[ckpt[c]] = Hc.astype(np.float32)
+    if ckpt_states is not None:
+        ckpt_states.update(stored)
     return o, new_pool, finals
 
 

@@ -450,6 +450,35 @@ def test_verify_in_place_first_position_reads_original():
     assert _nrm_err(states[(0, 2)], H_r) < 1e-13
 
 
+def test_prefill_checkpoints_equal_chunk_form_of_each_prefix():
+    """A checkpoint after chunk j holds the state after the first
+    min(64 (j + 1), len) tokens: the chunk form run on that prefix (another
+    algorithm) agrees, and outputs, finals and other slots do not change."""
+    rng = np.random.default_rng(17)
+    lengths = [150, 0, 64, 70]
+    pool, cu, q, k, v, g, b = _rand_prefill(rng, lengths, HK=1, HV=2, dk=6, dv=4, num_slots=16)
+    src = np.array([1, 2, -1, 3]); dst = np.array([4, 5, 6, -1])
+    nchunks = [(n + 63) // 64 for n in lengths]               # 3, 0, 1, 2
+    ckpt = -np.ones(sum(nchunks), np.int64)
+    ckpt[0], ckpt[2], ckpt[3], ckpt[4] = 10, 11, 12, 13       # seq 0 chunks 0 and 2, seq 2 chunk 0, seq 3 (skipped)
+    states = {}
+    o, new, fin = prefill(pool, cu, src, dst, q, k, v, g, b, 0.5, 1e-6, ckpt=ckpt, ckpt_states=states)
+    o0, new0, fin0 = prefill(pool, cu, src, dst, q, k, v, g, b, 0.5, 1e-6)
+    np.testing.assert_array_equal(np.nan_to_num(o, nan=9.0), np.nan_to_num(o0, nan=9.0))
+    for n in fin0:
+        assert _nrm_err(fin[n], fin0[n]) < 1e-13
+    assert set(states) == {0, 2, 3}                           # the skipped sequence stores nothing
+    cases = {0: (0, 64), 2: (0, 150), 3: (2, 64)}            # chunk -> (sequence, prefix length)
+    for c, (n, L) in cases.items():
+        a = cu[n]
+        H0 = pool[src[n]].astype(np.float64) if src[n] >= 0 else np.zeros(pool.shape[1:])
+        _, Hc = chunked_sequence(H0, q[a:a + L], k[a:a + L], v[a:a + L], g[a:a + L], b[a:a + L], 0.5, 1e-6, 16)
+        assert _nrm_err(states[c], Hc) < 1e-12
+        np.testing.assert_array_equal(new[ckpt[c]], states[c].astype(np.float32))
+    keep = [s for s in range(16) if s not in (4, 5, 6, 10, 11, 12)]
+    np.testing.assert_array_equal(new[keep], pool[keep])
+
+
 # ---------------------------------------------------------------------------
 # state hand-over (pack / unpack)
 # ---------------------------------------------------------------------------
