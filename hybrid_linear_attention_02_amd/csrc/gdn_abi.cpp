@@ -254,7 +254,7 @@ extern "C" int gdn_prefill_chunked(const gdn_pool* pool, const gdn_prefill_args*
     const void* vec[] = {a->q, a->k, a->v, a->o};
     for (const void* p : vec)
         if (!aligned(p, 16)) return fail(GDN_E_INVALID, "gdn_prefill_chunked: q, k, v, o must be 16-byte aligned");
-    const void* word[] = {a->g, a->beta, a->src_slots, a->dst_slots, a->err_flag, a->cu_seqlens};
+    const void* word[] = {a->g, a->beta, a->src_slots, a->dst_slots, a->err_flag, a->cu_seqlens, a->ckpt_slots};
     for (const void* p : word)
         if (!aligned(p, 4)) return fail(GDN_E_INVALID, "gdn_prefill_chunked: g, beta, tables, err_flag must be 4-byte aligned");
     if (workspace == nullptr || !aligned(workspace, 256))

@@ -80,6 +80,7 @@ struct PrefillParams {
     const int32_t* src;
     const int32_t* dst;
     int32_t* err;
+    const int32_t* ckpt;        // [chunks] device or null: slot receiving the state after each chunk
     uint16_t* tp;               // [chunks][HV][2][64 * 64] T, then P, as row-operand fragments
     float* sc;                  // [chunks][HV][5][64]    scale rows
     int32_t* chunk_off_w;       // same buffer as chunk_off, written by the prep kernel
@@ -978,12 +979,33 @@ prefill_recurrent_kernel(PrefillParams p) {
         }
         return;
     }
+    // periodic checkpoint: the state after chunk c0 + s, when one is requested
+    auto checkpoint = [&](int s) {
+        if (!OUT || p.ckpt == nullptr) return;
+        const int ck = p.ckpt[c0 + s];
+        if (ck < 0) return;
+        if (ck >= p.num_slots) {
+            if (tid == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
+            return;
+        }
+        float* out = p.pool + (static_cast<size_t>(ck) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[(16 * mu + 4 * g4 + i) * p.dv + col] = H[mu][i];
+    };
     if (steps > 0) lds_barrier();
     for (int s = 0; s < steps; s += 2) {
-        if (s < nch) chunk(0);
+        if (s < nch) {
+            chunk(0);
+            checkpoint(s);
+        }
         lds_barrier();
         if (s + 1 < steps) {
-            if (s + 1 < nch) chunk(1);
+            if (s + 1 < nch) {
+                chunk(1);
+                checkpoint(s + 1);
+            }
             lds_barrier();
         }
     }
@@ -1178,6 +1200,7 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
     p.src = a->src_slots;
     p.dst = a->dst_slots;
     p.err = a->err_flag;
+    p.ckpt = a->ckpt_slots;
     p.tp = reinterpret_cast<uint16_t*>(ws + plan.off_tp);
     p.sc = reinterpret_cast<float*>(ws + plan.off_sc);
     p.seg_off = reinterpret_cast<const int32_t*>(ws + plan.off_seg_offsets);

@@ -77,7 +77,7 @@ class PrefillArgs(ctypes.Structure):
         ("dk", c_int32), ("dv", c_int32), ("dtype", c_int32),
         ("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("g", c_void_p), ("beta", c_void_p),
         ("o", c_void_p), ("src_slots", c_void_p), ("dst_slots", c_void_p),
-        ("scale", c_float), ("l2_eps", c_float), ("err_flag", c_void_p),
+        ("scale", c_float), ("l2_eps", c_float), ("err_flag", c_void_p), ("ckpt_slots", c_void_p),
     ]
 
 
@@ -370,7 +370,7 @@ def gdn_decode_verify(pool: StatePool, q, k, v, g, beta, o, src_slots, dst_slots
 
 
 def _prefill_args(pool, q, k, v, g, beta, o, cu_seqlens, cu_seqlens_host, src_slots, dst_slots,
-                  scale, l2_eps, err_flag):
+                  scale, l2_eps, err_flag, ckpt_slots=None):
     import torch
     T, HK, dk = q.shape
     HV, dv = v.shape[1], v.shape[2]
@@ -391,6 +391,11 @@ def _prefill_args(pool, q, k, v, g, beta, o, cu_seqlens, cu_seqlens_host, src_sl
     a.scale = float(dk ** -0.5 if scale is None else scale)
     a.l2_eps = float(l2_eps)
     a.err_flag = _dev(err_flag, "err_flag", torch.int32)
+    if ckpt_slots is not None:
+        nchunks = int(np.sum((np.diff(host.astype(np.int64)) + 63) // 64))
+        if ckpt_slots.numel() != nchunks:
+            raise ValueError(f"ckpt_slots must have {nchunks} entries (one per 64-token chunk)")
+        a.ckpt_slots = _dev(ckpt_slots, "ckpt_slots", torch.int32)
     return a, host
 
 
@@ -404,15 +409,17 @@ def gdn_prefill_workspace_bytes(pool: StatePool, q, v, cu_seqlens_host) -> int:
 
 def gdn_prefill_chunked(pool: StatePool, q, k, v, g, beta, o, cu_seqlens, cu_seqlens_host, src_slots,
                         dst_slots, *, workspace=None, scale=None, l2_eps: float = 1e-6, err_flag=None,
-                        stream=None):
+                        ckpt_slots=None, stream=None):
     """Varlen chunked prefill. q, k: [T, HK, dk] bf16; v, o: [T, HV, dv] bf16;
     g, beta: float32 [T, HV]; cu_seqlens: int32 device [N+1] with its host
     mirror; src/dst: int32 device [N]. ``workspace``: a uint8 device tensor of
-    at least gdn_prefill_workspace_bytes (allocated here if None). Returns the
+    at least gdn_prefill_workspace_bytes (allocated here if None).
+    ``ckpt_slots``: optional int32 device [sum ceil(len / 64)], the slot that
+    receives the state after each 64-token chunk (-1: none). Returns the
     workspace tensor so callers can reuse it."""
     import torch
     a, host = _prefill_args(pool, q, k, v, g, beta, o, cu_seqlens, cu_seqlens_host, src_slots, dst_slots,
-                            scale, l2_eps, err_flag)
+                            scale, l2_eps, err_flag, ckpt_slots)
     n = c_size_t()
     _check(load_library().gdn_prefill_workspace_bytes(c_void_p(pool.handle), byref(a), byref(n)))
     if workspace is None:

@@ -240,6 +240,10 @@ typedef struct gdn_prefill_args {
     float scale;
     float l2_eps;
     int32_t* err_flag;            /* optional, as for decode */
+    const int32_t* ckpt_slots;    /* optional [C] device, C = sum over sequences of ceil(len / 64)
+                                     (sequence order, skipped sequences included): when
+                                     ckpt_slots[c] >= 0 the state after chunk c is also stored
+                                     to that slot (NULL: no checkpoints) */
 } gdn_prefill_args;
 
 /* Bytes of device workspace gdn_prefill_chunked needs for these args (depends
@@ -247,7 +251,14 @@ typedef struct gdn_prefill_args {
 int gdn_prefill_workspace_bytes(const gdn_pool* pool, const gdn_prefill_args* args, size_t* bytes);
 
 /* Run every sequence through the rule from its source state and write the
- * final state to its destination slot. Chunks of 64 tokens restart at every
+ * final state to its destination slot. With ckpt_slots the states at the
+ * chosen 64-token chunk boundaries are stored as well: the periodic
+ * checkpoints of the pages' hybrid prefix caching, which keeps the
+ * linear-attention state beside the KV pages (24-ai.news, English, section
+ * "What are the key optimizations behind the record?", item "Hybrid prefix
+ * caching for GDN/Mamba"). Checkpoint slots must be distinct and differ from
+ * every source and destination of the call; an out-of-range one is skipped
+ * and flagged. Chunks of 64 tokens restart at every
  * sequence boundary; a zero-length sequence copies the source state (zero if
  * src < 0) to the destination. `workspace` is caller-owned device memory of
  * at least gdn_prefill_workspace_bytes, 256-byte aligned; its contents are

@@ -306,3 +306,85 @@ def test_split_dk_ne_dv():
                           num_slots=3, pool_sigma=0.05, src=src, g_range=(1e-3, 5e-2))
     o, st, _ = _gpu_prefill(pw, src, dst)
     _check(pw, o, st, src, dst)
+
+
+def _gpu_prefill_ckpt(pw, src, dst, ckpt, err=None):
+    torch = _torch()
+    tk = pw.tokens
+    storage = torch.from_numpy(pw.pool.copy()).cuda()
+    pool = gdn.gdn_state_pool_create(pw.num_slots, pw.HV, pw.dk, pw.dv, storage=storage)
+    q, k, v = to_dev(tk.q, BF16), to_dev(tk.k, BF16), to_dev(tk.v, BF16)
+    o = torch.full(v.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    cu = torch.from_numpy(pw.cu_seqlens).cuda()
+    gdn.gdn_prefill_chunked(pool, q, k, v, to_dev(tk.g, "f32"), to_dev(tk.beta, "f32"), o, cu, pw.cu_seqlens,
+                            torch.tensor(src, dtype=torch.int32, device="cuda"),
+                            torch.tensor(dst, dtype=torch.int32, device="cuda"),
+                            scale=pw.dk ** -0.5, l2_eps=EPS, err_flag=err,
+                            ckpt_slots=torch.tensor(ckpt, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    pool.close()
+    return o, storage
+
+
+def _check_ckpt(pw, o, storage, src, dst, ckpt):
+    tk = pw.tokens
+    states = {}
+    o_ref, _, fin = oracle_prefill(pw.pool, pw.cu_seqlens, src, dst, as_f64(tk.q, BF16), as_f64(tk.k, BF16),
+                                   as_f64(tk.v, BF16), tk.g, tk.beta, pw.dk ** -0.5, EPS, ckpt=ckpt,
+                                   ckpt_states=states)
+    got = storage.cpu().numpy()
+    og = out_f64(o)
+    for n in range(len(src)):
+        a, b = pw.cu_seqlens[n], pw.cu_seqlens[n + 1]
+        if dst[n] >= 0 and b > a:
+            check_outputs(og[a:b], o_ref[a:b], BF16, f"seq {n}")
+            check_state(got[dst[n]], fin[n], BF16, f"seq {n} final")
+    for c, H in states.items():
+        check_state(got[ckpt[c]], H, BF16, f"checkpoint after chunk {c}")
+    return states, got
+
+
+def test_prefill_checkpoints_varlen():
+    """Checkpoints after chosen chunks of ragged sequences (including a
+    sequence's last, partial chunk, a skipped sequence's chunk and an empty
+    sequence): every stored state matches the oracle's state after that
+    chunk, nothing else changes."""
+    lengths = [150, 0, 64, 70, 200]
+    src = [0, 1, -1, 2, 3]
+    dst = [4, 5, 6, -1, 7]
+    nchunks = [(n + 63) // 64 for n in lengths]              # 3, 0, 1, 2, 4 -> 10
+    ckpt = [-1] * sum(nchunks)
+    ckpt[0], ckpt[2], ckpt[3], ckpt[5], ckpt[6], ckpt[8] = 8, 9, 10, 11, 12, 13
+    pw = prefill_workload("ckpt_varlen", seed=81, lengths=lengths, HK=2, HV=4, dk=128, dv=64, dtype=BF16,
+                          num_slots=16, pool_sigma=0.05, src=src, g_range=(1e-3, 0.1))
+    o, st = _gpu_prefill_ckpt(pw, src, dst, ckpt)
+    states, got = _check_ckpt(pw, o, st, src, dst, ckpt)
+    assert set(states) == {0, 2, 3, 6, 8}                    # chunk 5 belongs to the skipped sequence
+    untouched = [s for s in range(16) if s not in (4, 5, 6, 7, 8, 9, 10, 12, 13)]
+    np.testing.assert_array_equal(got[untouched], pw.pool[untouched])
+
+
+def test_prefill_checkpoints_on_split_sequence():
+    """A sequence long enough to be split into segments, with checkpoints on
+    both sides of segment boundaries, from a source slot."""
+    T = 3000
+    pw = prefill_workload("ckpt_split", seed=82, lengths=[T], HK=2, HV=4, dk=128, dv=128, dtype=BF16,
+                          num_slots=24, pool_sigma=0.05, src=[0], g_range=(1e-3, 0.05))
+    nch = (T + 63) // 64                                      # 47
+    ckpt = [-1] * nch
+    for i, c in enumerate([0, 7, 15, 16, 23, 24, 31, 40, 46]):
+        ckpt[c] = 2 + i
+    o, st = _gpu_prefill_ckpt(pw, [0], [1], ckpt)
+    states, got = _check_ckpt(pw, o, st, [0], [1], ckpt)
+    assert len(states) == 9
+    np.testing.assert_array_equal(got[0], pw.pool[0])
+
+
+def test_prefill_checkpoint_out_of_range_is_flagged():
+    torch = _torch()
+    pw = prefill_workload("ckpt_flag", seed=83, lengths=[130], HK=1, HV=2, dk=64, dv=64, dtype=BF16,
+                          num_slots=4, pool_sigma=0.05, src=[0])
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o, st = _gpu_prefill_ckpt(pw, [0], [1], [2, 99, -1], err=err)
+    assert int(err.item()) == gdn.GDN_ERRFLAG_SLOT_RANGE
+    _check_ckpt(pw, o, st, [0], [1], [2, -1, -1])
