@@ -23,4 +23,5 @@ from .gdn_oracle import (  # noqa: F401
     state_pack,
     state_unpack,
     SlotPoolModel,
+    PrefixCacheModel,
 )

@@ -459,3 +459,68 @@ class SlotPoolModel:
                 if j != i and s == d:
                     return GDN_E_ALIAS
         return GDN_OK
+
+
+class PrefixCacheModel:
+    """Reference model of the logical prefix cache (the pages' C++ layer of
+    hybrid prefix caching with radix-tree matching over linear-attention
+    state slots: 24-ai.news (English), section "What are the key
+    optimizations behind the record?", item "Hybrid prefix caching for
+    GDN/Mamba"). A plain dict from token prefix to [slot, stamp] over a
+    SlotPoolModel: the tree only makes the same answers fast.
+
+    insert: the prefix gets the slot (the cache retains it) unless it already
+    has one. match: the longest stored prefix of the tokens; a hit retains
+    its slot for the caller and restamps it. evict: drop the checkpoints whose
+    slot only the cache holds (refcount 1), oldest stamp first, until the pool
+    has `want_free` free slots. Stamps come from one clock advanced by every
+    insert and every hit.
+    """
+
+    def __init__(self, pool_model):
+        self.pool = pool_model
+        self.entries = {}
+        self.clock = 0
+
+    def insert(self, tokens, slot):
+        key = tuple(int(t) for t in tokens)
+        if len(key) == 0 or slot < 0 or slot >= self.pool.capacity:
+            return GDN_E_INVALID, 0
+        if self.pool.refcount(slot)[1] == 0:
+            return GDN_E_SLOT_STATE, 0
+        if key in self.entries:
+            return GDN_OK, 0
+        self.pool.retain(slot)
+        self.clock += 1
+        self.entries[key] = [slot, self.clock]
+        return GDN_OK, 1
+
+    def match(self, tokens):
+        toks = tuple(int(t) for t in tokens)
+        best = None
+        for key in self.entries:
+            if len(key) <= len(toks) and toks[:len(key)] == key and (best is None or len(key) > len(best)):
+                best = key
+        if best is None:
+            return GDN_OK, 0, -1
+        slot = self.entries[best][0]
+        self.pool.retain(slot)
+        self.clock += 1
+        self.entries[best][1] = self.clock
+        return GDN_OK, len(best), slot
+
+    def evict(self, want_free):
+        dropped = 0
+        for key in sorted(self.entries, key=lambda k: self.entries[k][1]):
+            if self.pool.num_free() >= want_free:
+                break
+            slot = self.entries[key][0]
+            if self.pool.refcount(slot)[1] != 1:
+                continue
+            self.pool.release(slot)
+            del self.entries[key]
+            dropped += 1
+        return GDN_OK, dropped
+
+    def size(self):
+        return len(self.entries)
