@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_pool.cpp", "gdn_abi.cpp", "gdn_decode.hip", "gdn_prefill.hip", "gdn_transfer.hip"]
+SOURCES = ["gdn_pool.cpp", "gdn_abi.cpp", "gdn_prefix_cache.cpp", "gdn_decode.hip", "gdn_prefill.hip",
+           "gdn_transfer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

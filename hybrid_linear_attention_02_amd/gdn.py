@@ -39,7 +39,8 @@ EXPORTED = (
     "gdn_state_pool_validate", "gdn_state_pool_refcount", "gdn_state_pool_num_free",
     "gdn_state_pool_capacity", "gdn_decode_step", "gdn_prefill_workspace_bytes",
     "gdn_decode_verify", "gdn_prefill_chunked", "gdn_last_error", "gdn_state_pool_pack",
-    "gdn_state_pool_unpack",
+    "gdn_state_pool_unpack", "gdn_prefix_cache_create", "gdn_prefix_cache_destroy", "gdn_prefix_cache_insert",
+    "gdn_prefix_cache_match", "gdn_prefix_cache_evict", "gdn_prefix_cache_size",
 )
 
 
@@ -106,6 +107,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_state_pool_refcount": ([P, c_int32, POINTER(c_int32)], c_int32),
         "gdn_state_pool_num_free": ([P, POINTER(c_int32)], c_int32),
         "gdn_state_pool_capacity": ([P, POINTER(c_int32)], c_int32),
+        "gdn_prefix_cache_create": ([P, POINTER(P)], c_int32),
+        "gdn_prefix_cache_destroy": ([P], c_int32),
+        "gdn_prefix_cache_insert": ([P, POINTER(c_int32), c_int32, c_int32, POINTER(c_int32)], c_int32),
+        "gdn_prefix_cache_match": ([P, POINTER(c_int32), c_int32, POINTER(c_int32), POINTER(c_int32)], c_int32),
+        "gdn_prefix_cache_evict": ([P, c_int32, POINTER(c_int32)], c_int32),
+        "gdn_prefix_cache_size": ([P, POINTER(c_int32)], c_int32),
         "gdn_state_pool_pack": ([P, c_int32, P, P, P, P], c_int32),
         "gdn_state_pool_unpack": ([P, c_int32, P, P, P, P], c_int32),
         "gdn_decode_step": ([P, POINTER(DecodeArgs), P], c_int32),
@@ -308,6 +315,59 @@ def gdn_decode_step(pool: StatePool, q, k, v, g, beta, o, src_slots, dst_slots, 
     a.l2_eps = float(l2_eps)
     a.err_flag = _dev(err_flag, "err_flag", torch.int32)
     _check(load_library().gdn_decode_step(c_void_p(pool.handle), byref(a), _stream(stream)))
+
+
+class PrefixCache:
+    """Radix tree over token ids whose nodes own slot checkpoints of `pool`
+    (the C library's logical prefix cache). Close it before the pool."""
+
+    def __init__(self, pool: StatePool):
+        h = c_void_p()
+        _check(load_library().gdn_prefix_cache_create(c_void_p(pool.handle), byref(h)))
+        self.handle = h.value
+        self.pool = pool
+
+    @staticmethod
+    def _tokens(tokens):
+        t = np.ascontiguousarray(np.asarray(tokens, np.int32))
+        return t, t.ctypes.data_as(POINTER(c_int32))
+
+    def insert(self, tokens, slot: int) -> bool:
+        """The cache retains `slot` as the state after `tokens`; False if that
+        prefix already had a checkpoint (nothing changes then)."""
+        t, ptr = self._tokens(tokens)
+        out = c_int32()
+        _check(load_library().gdn_prefix_cache_insert(c_void_p(self.handle), ptr, len(t), int(slot), byref(out)))
+        return bool(out.value)
+
+    def match(self, tokens):
+        """(length, slot) of the longest checkpointed prefix, (0, -1) on a
+        miss; a hit retains the slot for the caller."""
+        t, ptr = self._tokens(tokens)
+        n, s = c_int32(), c_int32()
+        _check(load_library().gdn_prefix_cache_match(c_void_p(self.handle), ptr, len(t), byref(n), byref(s)))
+        return n.value, s.value
+
+    def evict(self, want_free: int) -> int:
+        out = c_int32()
+        _check(load_library().gdn_prefix_cache_evict(c_void_p(self.handle), int(want_free), byref(out)))
+        return out.value
+
+    def size(self) -> int:
+        out = c_int32()
+        _check(load_library().gdn_prefix_cache_size(c_void_p(self.handle), byref(out)))
+        return out.value
+
+    def close(self) -> None:
+        if self.handle:
+            load_library().gdn_prefix_cache_destroy(c_void_p(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def gdn_state_pool_pack(pool: StatePool, slots, buffer, *, err_flag=None, stream=None) -> None:

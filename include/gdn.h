@@ -120,6 +120,43 @@ int gdn_state_pool_num_free(const gdn_pool* pool, int32_t* out);
 int gdn_state_pool_capacity(const gdn_pool* pool, int32_t* out);
 
 /* ------------------------------------------------------------------------ */
+/* prefix cache: the logical layer over slot checkpoints                     */
+/* ------------------------------------------------------------------------ */
+
+/* 24-ai.news (English), section "What are the key optimizations behind the
+ * record?", item "Hybrid prefix caching for GDN/Mamba": context caching is
+ * split between a C++ logical cache and the physical tensors, with radix-tree
+ * matching extended to the linear-attention state slots and copy-on-write
+ * reuse. This is that logical layer for one pool: a radix tree over token ids
+ * whose nodes own slot checkpoints (a slot holding the state after exactly
+ * that prefix, written e.g. by a prefill checkpoint). The cache holds one
+ * reference (refcount) on every slot it owns; callers keep their own. Not
+ * thread-safe, like the pool. Errors: GDN_E_INVALID (NULL, n <= 0, slot out
+ * of range), GDN_E_SLOT_STATE (a free slot), GDN_E_NO_SLOTS (create: none). */
+typedef struct gdn_prefix_cache gdn_prefix_cache;
+
+/* A cache over `pool`, which must outlive it. */
+int gdn_prefix_cache_create(gdn_pool* pool, gdn_prefix_cache** out);
+/* Releases every checkpoint's reference, then frees the cache. NULL is a no-op. */
+int gdn_prefix_cache_destroy(gdn_prefix_cache* cache);
+/* Record that allocated `slot` holds the state after tokens[0..n). The cache
+ * retains it (*inserted = 1). If that prefix already has a checkpoint nothing
+ * changes (*inserted = 0; the caller keeps its own reference either way). */
+int gdn_prefix_cache_insert(gdn_prefix_cache* cache, const int32_t* tokens, int32_t n, int32_t slot,
+                            int32_t* inserted);
+/* Longest prefix of tokens[0..n) that has a checkpoint: *len tokens in slot
+ * *slot, retained once more for the caller (who releases it when done) and
+ * marked most recently used; *len = 0 and *slot = -1 on a miss. A request
+ * resumes from it copy-on-write: read the slot as its source, write elsewhere. */
+int gdn_prefix_cache_match(gdn_prefix_cache* cache, const int32_t* tokens, int32_t n, int32_t* len, int32_t* slot);
+/* Drop checkpoints whose slot the cache alone holds (refcount 1), least
+ * recently inserted or matched first, until the pool has at least
+ * `want_free` free slots or no such checkpoint is left. *dropped = how many. */
+int gdn_prefix_cache_evict(gdn_prefix_cache* cache, int32_t want_free, int32_t* dropped);
+/* Number of checkpoints held. */
+int gdn_prefix_cache_size(const gdn_prefix_cache* cache, int32_t* out);
+
+/* ------------------------------------------------------------------------ */
 /* state transfer                                                            */
 /* ------------------------------------------------------------------------ */
 
