@@ -354,6 +354,126 @@ def bench_transfer(reps=20):
             "unpack_us": tu * 1e6, "unpack_gbs": 2 * nbytes / tu / 1e9}
 
 
+def bench_graph(reps=200, warmup=20):
+    """Launch overhead of a whole decode step: the same decode launches made
+    one by one through the Python binding ("binding", what a Python-driven
+    scheduler pays per launch), through the C ABI with prebuilt argument
+    structs ("eager"), and replayed as one recorded graph. Rates are wall-clock
+    over `reps` back-to-back steps, host launch cost included.
+      tiny_chain: the tiny fp32 workload's 8 sequential tokens (1 request,
+        2 value heads, 16 x 16), slot 1 -> 2 then in place;
+      stack_b{B}: one token through 32 GDN layers (own storages, in place) at
+        16/32 heads, 128 x 128 bf16, for B = 1 and 8 requests."""
+    import ctypes
+    import time
+    import torch
+    from hybrid_linear_attention_02_amd import gdn
+    from hybrid_linear_attention_02_amd.workloads import BF16, decode_workload, tiny_decode
+
+    lib = gdn.load_library()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def dev(x, dt):
+        if dt == BF16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    def run(pool, entries, storages):
+        keep = []
+        args = [gdn.decode_args(*e, err_flag=err) for e in entries]
+        graph = gdn.DecodeGraph(pool, args, storages=storages, keep=entries)
+        handle = ctypes.c_void_p(pool.handle)
+        eager_pools, pool_objs = [], []
+        for t in (storages or [None] * len(entries)):
+            if t is None:
+                eager_pools.append(handle)
+                pool_objs.append(pool)
+            else:
+                p = gdn.gdn_state_pool_create(pool.num_slots, pool.num_v_heads, pool.dk, pool.dv, storage=t)
+                p.alloc(pool.num_slots)
+                keep.append(p)
+                eager_pools.append(ctypes.c_void_p(p.handle))
+                pool_objs.append(p)
+        refs = [ctypes.byref(a) for a in args]
+
+        def binding():
+            for p, e in zip(pool_objs, entries):
+                gdn.gdn_decode_step(p, *e, err_flag=err)
+
+        def eager():
+            for h, a in zip(eager_pools, refs):
+                if lib.gdn_decode_step(h, a, sp) != 0:
+                    raise RuntimeError(gdn.gdn_last_error())
+
+        gh = ctypes.c_void_p(graph.handle)
+
+        def replay():
+            if lib.gdn_decode_graph_launch(gh, sp) != 0:
+                raise RuntimeError(gdn.gdn_last_error())
+
+        out = {}
+        for name, fn in (("binding", binding), ("eager", eager), ("graph", replay)):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn()
+            torch.cuda.synchronize()
+            out[name] = (time.perf_counter() - t0) / reps
+        n, f = graph.poll()
+        assert n == warmup + reps and f == 0, (n, f)
+        assert int(err.item()) == 0
+        graph.close()
+        for p in keep:
+            p.close()
+        return out
+
+    res = {}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # tiny chain
+    wl = tiny_decode(steps=8)
+    storage = torch.from_numpy(wl.pool.copy()).cuda()
+    pool = gdn.gdn_state_pool_create(wl.num_slots, wl.HV, wl.dk, wl.dv, storage=storage)
+    pool.alloc(wl.num_slots)
+    t1, t2, t22 = [torch.tensor([x], dtype=torch.int32, device="cuda") for x in (1, 2, 2)]
+    entries = []
+    for i, tk in enumerate(wl.steps):
+        q, k, v = dev(tk.q, wl.dtype), dev(tk.k, wl.dtype), dev(tk.v, wl.dtype)
+        entries.append((q, k, v, dev(tk.g, None), dev(tk.beta, None), torch.empty_like(v),
+                        t1 if i == 0 else t22, t2 if i == 0 else t22))
+    r = run(pool, entries, None)
+    res["tiny_chain_8_tokens"] = {"binding_us_per_token": r["binding"] / 8 * 1e6,
+                                  "eager_us_per_token": r["eager"] / 8 * 1e6,
+                                  "graph_us_per_token": r["graph"] / 8 * 1e6,
+                                  "speedup": r["eager"] / r["graph"],
+                                  "speedup_vs_binding": r["binding"] / r["graph"]}
+    pool.close()
+    # layer stacks
+    L = 32
+    for B in (1, 8):
+        wl = decode_workload(f"stack_b{B}", seed=60 + B, B=B, HK=16, HV=32, dk=128, dv=128, dtype=BF16,
+                             num_slots=B, pool_sigma=0.05, steps=1)
+        tk = wl.steps[0]
+        pool = gdn.gdn_state_pool_create(B, 32, 128, 128)
+        pool.alloc(B)
+        slots = torch.arange(B, dtype=torch.int32, device="cuda")
+        q, k, v = dev(tk.q, BF16), dev(tk.k, BF16), dev(tk.v, BF16)
+        g, beta = dev(tk.g, None), dev(tk.beta, None)
+        storages = [torch.from_numpy(wl.pool).cuda() for _ in range(L)]
+        entries = [(q, k, v, g, beta, torch.empty_like(v), slots, slots) for _ in range(L)]
+        r = run(pool, entries, storages)
+        res[f"stack_b{B}_32_layers"] = {"binding_us_per_step": r["binding"] * 1e6,
+                                        "eager_us_per_step": r["eager"] * 1e6, "graph_us_per_step": r["graph"] * 1e6,
+                                        "graph_us_per_layer": r["graph"] / L * 1e6,
+                                        "speedup": r["eager"] / r["graph"],
+                                        "speedup_vs_binding": r["binding"] / r["graph"]}
+        pool.close()
+        del storages
+    return {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in res.items()}
+
+
 def _oracle_worker(args):
     os.environ["OMP_NUM_THREADS"] = "1"
     (pool_part, src, dst, steps_part, scale, repeats) = args
@@ -576,6 +696,7 @@ def main():
         pre["cpu_baseline"] = cpu_pre
     ver = bench_verify()
     xfer = bench_transfer()
+    grf = bench_graph()
     ach = achievable()
     line = {
         "metric": METRIC,
@@ -610,6 +731,7 @@ def main():
         "achievable": ach,
         "verify": ver,
         "transfer": xfer,
+        "decode_graph": grf,
         "prefill": pre,
     }
     print(json.dumps(line))

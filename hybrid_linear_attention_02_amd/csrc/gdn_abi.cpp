@@ -50,28 +50,39 @@ extern "C" int gdn_state_pool_unpack(const gdn_pool* pool, int32_t n, const int3
     return transfer(pool, false, n, slots, buffer, err_flag, stream);
 }
 
-extern "C" int gdn_decode_step(const gdn_pool* pool, const gdn_decode_args* a, void* stream) {
-    const char* fn = "gdn_decode_step";
-    if (pool == nullptr || a == nullptr) return fail(GDN_E_INVALID, "gdn_decode_step: NULL pool or args");
-    if (a->batch < 0) return fail(GDN_E_INVALID, "gdn_decode_step: batch must be >= 0");
-    int st = check_heads(pool, a->num_k_heads, a->num_v_heads, a->dk, a->dv, fn);
+namespace gdn {
+
+// Checks of one decode step's arguments, shared by gdn_decode_step and the
+// recorded decode graph. GDN_OK for batch == 0 without looking at pointers.
+int check_decode_args(const gdn_pool* pool, const gdn_decode_args* a, const char* fn) {
+    if (pool == nullptr || a == nullptr) return fail(GDN_E_INVALID, std::string(fn) + ": NULL pool or args");
+    if (a->batch < 0) return fail(GDN_E_INVALID, std::string(fn) + ": batch must be >= 0");
+    const int st = check_heads(pool, a->num_k_heads, a->num_v_heads, a->dk, a->dv, fn);
     if (st != GDN_OK) return st;
     if (a->dtype != GDN_DTYPE_F32 && a->dtype != GDN_DTYPE_BF16)
-        return fail(GDN_E_UNSUPPORTED, "gdn_decode_step: dtype must be GDN_DTYPE_F32 or GDN_DTYPE_BF16");
+        return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": dtype must be GDN_DTYPE_F32 or GDN_DTYPE_BF16");
     if (!std::isfinite(a->scale) || !(a->l2_eps >= 0.0f) || !std::isfinite(a->l2_eps))
-        return fail(GDN_E_INVALID, "gdn_decode_step: scale must be finite and l2_eps finite and >= 0");
+        return fail(GDN_E_INVALID, std::string(fn) + ": scale must be finite and l2_eps finite and >= 0");
     if (static_cast<int64_t>(a->batch) * a->num_v_heads > INT32_MAX)
-        return fail(GDN_E_INVALID, "gdn_decode_step: batch * num_v_heads too large");
+        return fail(GDN_E_INVALID, std::string(fn) + ": batch * num_v_heads too large");
     if (a->batch == 0) return GDN_OK;
     const void* ptrs[] = {a->q, a->k, a->v, a->g, a->beta, a->o, a->src_slots, a->dst_slots};
     for (const void* p : ptrs)
-        if (p == nullptr) return fail(GDN_E_INVALID, "gdn_decode_step: NULL device pointer");
+        if (p == nullptr) return fail(GDN_E_INVALID, std::string(fn) + ": NULL device pointer");
     const void* vec[] = {a->q, a->k, a->v, a->o};
     for (const void* p : vec)
-        if (!aligned(p, 16)) return fail(GDN_E_INVALID, "gdn_decode_step: q, k, v, o must be 16-byte aligned");
+        if (!aligned(p, 16)) return fail(GDN_E_INVALID, std::string(fn) + ": q, k, v, o must be 16-byte aligned");
     const void* word[] = {a->g, a->beta, a->src_slots, a->dst_slots, a->err_flag};
     for (const void* p : word)
-        if (!aligned(p, 4)) return fail(GDN_E_INVALID, "gdn_decode_step: g, beta, slot tables, err_flag must be 4-byte aligned");
+        if (!aligned(p, 4)) return fail(GDN_E_INVALID, std::string(fn) + ": g, beta, slot tables, err_flag must be 4-byte aligned");
+    return GDN_OK;
+}
+
+}  // namespace gdn
+
+extern "C" int gdn_decode_step(const gdn_pool* pool, const gdn_decode_args* a, void* stream) {
+    const int st = gdn::check_decode_args(pool, a, "gdn_decode_step");
+    if (st != GDN_OK || a->batch == 0) return st;
     return gdn::launch_decode(pool, a, stream);
 }
 

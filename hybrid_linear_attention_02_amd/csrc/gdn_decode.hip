@@ -363,9 +363,10 @@ DecodeParams make_params(const gdn_pool* pool, const A* a) {
 
 namespace gdn {
 
-int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream) {
+int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream, float* storage) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const DecodeParams p = make_params(pool, a);
+    DecodeParams p = make_params(pool, a);
+    if (storage != nullptr) p.pool = storage;
     if (a->dtype == GDN_DTYPE_F32) return dispatch_dv<float, false>(p, a->batch, a->dk, a->dv, s);
     return dispatch_dv<uint16_t, false>(p, a->batch, a->dk, a->dv, s);
 }

@@ -26,7 +26,11 @@ int fail(int code, const std::string& msg);
 
 // Kernel launchers (defined in the .hip files). They assume validated
 // arguments and return GDN_OK or GDN_E_HIP / GDN_E_UNSUPPORTED.
-int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream);
+// `storage` (when not NULL) replaces the pool's own slot storage: a tensor of
+// the same [slot][HV][dk][dv] shape, as one layer of a stack of GDN layers
+// that share the pool's slot numbering holds.
+int launch_decode(const gdn_pool* pool, const gdn_decode_args* a, void* stream, float* storage = nullptr);
+int check_decode_args(const gdn_pool* pool, const gdn_decode_args* a, const char* fn);
 constexpr int kMaxDraft = 64;     // draft tokens per request in one verify launch
 int launch_verify(const gdn_pool* pool, const gdn_verify_args* a, void* stream);
 int launch_transfer(const gdn_pool* pool, bool pack, int32_t n, const int32_t* slots, float* buffer,

@@ -41,7 +41,12 @@ EXPORTED = (
     "gdn_decode_verify", "gdn_prefill_chunked", "gdn_last_error", "gdn_state_pool_pack",
     "gdn_state_pool_unpack", "gdn_prefix_cache_create", "gdn_prefix_cache_destroy", "gdn_prefix_cache_insert",
     "gdn_prefix_cache_match", "gdn_prefix_cache_evict", "gdn_prefix_cache_size",
+    "gdn_decode_graph_create", "gdn_decode_graph_launch", "gdn_decode_graph_poll",
+    "gdn_decode_graph_wait_entry", "gdn_decode_graph_sync_entry", "gdn_decode_graph_destroy",
 )
+
+GDN_GRAPH_LAYER_EVENTS = 1
+GDN_GRAPH_MAX_ENTRIES = 4096
 
 
 class GdnError(RuntimeError):
@@ -119,6 +124,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_decode_verify": ([P, POINTER(VerifyArgs), P], c_int32),
         "gdn_prefill_workspace_bytes": ([P, POINTER(PrefillArgs), POINTER(c_size_t)], c_int32),
         "gdn_prefill_chunked": ([P, POINTER(PrefillArgs), P, c_size_t, P], c_int32),
+        "gdn_decode_graph_create": ([P, c_int32, POINTER(DecodeArgs), POINTER(P), c_int32, POINTER(P)], c_int32),
+        "gdn_decode_graph_launch": ([P, P], c_int32),
+        "gdn_decode_graph_poll": ([P, POINTER(ctypes.c_uint32), POINTER(c_int32)], c_int32),
+        "gdn_decode_graph_wait_entry": ([P, c_int32, P], c_int32),
+        "gdn_decode_graph_sync_entry": ([P, c_int32], c_int32),
+        "gdn_decode_graph_destroy": ([P], c_int32),
         "gdn_last_error": ([], c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -293,6 +304,15 @@ def gdn_decode_step(pool: StatePool, q, k, v, g, beta, o, src_slots, dst_slots, 
     """One decode token per request. q, k: [B, HK, dk]; v, o: [B, HV, dv]
     (all float32 or all bfloat16); g, beta: float32 [B, HV]; src/dst: int32
     device [B]. Enqueued on ``stream`` (default: the current stream)."""
+    a = decode_args(q, k, v, g, beta, o, src_slots, dst_slots, scale=scale, l2_eps=l2_eps, err_flag=err_flag)
+    _check(load_library().gdn_decode_step(c_void_p(pool.handle), byref(a), _stream(stream)))
+
+
+def decode_args(q, k, v, g, beta, o, src_slots, dst_slots, *, scale=None, l2_eps: float = 1e-6,
+                err_flag=None) -> DecodeArgs:
+    """The gdn_decode_args struct for these tensors (shapes as in
+    gdn_decode_step). The struct holds raw addresses: the tensors must stay
+    alive while it, or a graph recorded from it, is in use."""
     import torch
     B, HK, dk = q.shape
     HV, dv = v.shape[1], v.shape[2]
@@ -314,7 +334,57 @@ def gdn_decode_step(pool: StatePool, q, k, v, g, beta, o, src_slots, dst_slots, 
     a.scale = float(dk ** -0.5 if scale is None else scale)
     a.l2_eps = float(l2_eps)
     a.err_flag = _dev(err_flag, "err_flag", torch.int32)
-    _check(load_library().gdn_decode_step(c_void_p(pool.handle), byref(a), _stream(stream)))
+    return a
+
+
+class DecodeGraph:
+    """A recorded list of decode launches (gdn_decode_graph_*).
+
+    ``entries``: DecodeArgs structs (see decode_args), replayed in order;
+    ``storages``: optional list of float32 device tensors of the pool's shape
+    (None entries use the pool's storage). The graph keeps references to
+    ``keep`` (the tensors the structs point at) so they outlive it."""
+
+    def __init__(self, pool: StatePool, entries, storages=None, *, layer_events: bool = False, keep=()):
+        n = len(entries)
+        arr = (DecodeArgs * max(n, 1))(*entries)
+        st = None
+        if storages is not None:
+            if len(storages) != n:
+                raise ValueError("storages must have one entry per launch")
+            st = (c_void_p * n)(*[None if t is None else _dev(t, "storage") for t in storages])
+        h = c_void_p()
+        flags = GDN_GRAPH_LAYER_EVENTS if layer_events else 0
+        _check(load_library().gdn_decode_graph_create(c_void_p(pool.handle), n, arr, st, flags, byref(h)))
+        self.handle = h.value
+        self.num_entries = n
+        self._keep = (pool, list(keep), list(storages or []))
+
+    def launch(self, stream=None) -> None:
+        _check(load_library().gdn_decode_graph_launch(c_void_p(self.handle), _stream(stream)))
+
+    def poll(self):
+        """(replays finished, err_flag bits of the last one), read from host memory."""
+        n, f = ctypes.c_uint32(), c_int32()
+        _check(load_library().gdn_decode_graph_poll(c_void_p(self.handle), byref(n), byref(f)))
+        return int(n.value), int(f.value)
+
+    def wait_entry(self, entry: int, stream=None) -> None:
+        _check(load_library().gdn_decode_graph_wait_entry(c_void_p(self.handle), int(entry), _stream(stream)))
+
+    def sync_entry(self, entry: int) -> None:
+        _check(load_library().gdn_decode_graph_sync_entry(c_void_p(self.handle), int(entry)))
+
+    def close(self) -> None:
+        if self.handle:
+            load_library().gdn_decode_graph_destroy(c_void_p(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class PrefixCache:

@@ -65,7 +65,8 @@ extern "C" {
 #define GDN_DTYPE_F32  0
 #define GDN_DTYPE_BF16 1
 
-/* bits of the optional device error flag (int32, set by kernels, never cleared) */
+/* bits of the optional device error flag (int32, OR-ed in by kernels; only the
+ * end of a decode-graph replay clears it) */
 #define GDN_ERRFLAG_SLOT_RANGE 1   /* a src/dst slot index >= num_slots was skipped */
 #define GDN_ERRFLAG_DRAFT_LEN  2   /* a draft length outside [0, num_draft] was skipped (verify) */
 
@@ -253,6 +254,70 @@ typedef struct gdn_verify_args {
  * err_flag. Asynchronous on `stream`, no allocation, no host synchronisation,
  * graph-capturable. */
 int gdn_decode_verify(const gdn_pool* pool, const gdn_verify_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* recorded decode step: a whole step of decode launches as one HIP graph    */
+/* ------------------------------------------------------------------------ */
+
+/* The TokenSpeed article (24-ai.news, English, section "What are the key
+ * optimizations behind the record?", item "CUDA graph recording") records the
+ * whole decode loop as one graph so that kernels are not launched one by one;
+ * zubnet.ai (Portuguese), second paragraph, adds the overlap of host and GPU
+ * work around it: graph capture, asynchronous host-to-device copies from
+ * pinned memory, layer barriers built on events, and sentinels written by the
+ * GPU so the host need not read device memory back. Here:
+ *   - a list of decode launches ("entries", e.g. one per GDN layer of a model,
+ *     or several steps of one layer) is recorded once and replayed per step;
+ *   - the slot tables stay in device memory: every entry reads the src/dst
+ *     tables its args name, which the caller (or GPU code, e.g. an acceptance
+ *     kernel) rewrites between replays in stream order, typically by an
+ *     asynchronous copy from pinned host memory;
+ *   - each replay ends with a sentinel kernel that reads the shared err_flag,
+ *     clears it, counts the replay and writes (count, flags) into pinned host
+ *     memory, which gdn_decode_graph_poll reads without any GPU call;
+ *   - with GDN_GRAPH_LAYER_EVENTS an event is recorded after every entry, and
+ *     a stream or the host can wait for entry i of the latest replay alone. */
+
+typedef struct gdn_decode_graph gdn_decode_graph;   /* opaque */
+
+#define GDN_GRAPH_LAYER_EVENTS 1   /* record an event after every entry */
+#define GDN_GRAPH_MAX_ENTRIES 4096
+
+/* Record `num_entries` decode launches, in order, into a graph. entries[i] is
+ * checked as by gdn_decode_step and must have batch >= 1; every entry must
+ * name the same non-NULL err_flag. storages (optional, NULL = all entries use
+ * the pool's storage) gives entry i's slot storage: NULL for the pool's own,
+ * else device memory of the pool's shape [num_slots][HV][dk][dv] float32,
+ * 16-byte aligned (one GDN layer's states; all layers share the pool's slot
+ * numbering). Every pointer is baked into the graph: the buffers must outlive
+ * it, and their contents are read at each replay. flags: 0 or
+ * GDN_GRAPH_LAYER_EVENTS. The library allocates the graph, its events, a
+ * device word and a pinned host word; nothing is enqueued on caller streams.
+ * On failure nothing is left allocated and *out is unchanged. */
+int gdn_decode_graph_create(const gdn_pool* pool, int32_t num_entries, const gdn_decode_args* entries,
+                            float* const* storages, int32_t flags, gdn_decode_graph** out);
+
+/* Enqueue one replay on `stream`. Replays of one graph must not overlap:
+ * launch them on one stream, or order them. Asynchronous, no allocation. */
+int gdn_decode_graph_launch(gdn_decode_graph* graph, void* stream);
+
+/* Replays finished so far (the sentinel count, 0 before the first) and the
+ * err_flag bits the last of them saw. Host memory only: no GPU call, no
+ * synchronisation. A count behind the number of launches means a replay is
+ * still running. */
+int gdn_decode_graph_poll(const gdn_decode_graph* graph, uint32_t* replays, int32_t* flags);
+
+/* Make `stream` wait, on the GPU, until entry `entry` of the latest enqueued
+ * replay has finished (needs GDN_GRAPH_LAYER_EVENTS). */
+int gdn_decode_graph_wait_entry(const gdn_decode_graph* graph, int32_t entry, void* stream);
+
+/* Block the host until entry `entry` of the latest enqueued replay has
+ * finished (needs GDN_GRAPH_LAYER_EVENTS). */
+int gdn_decode_graph_sync_entry(const gdn_decode_graph* graph, int32_t entry);
+
+/* Wait for the device to go idle, then free the graph and everything the
+ * library allocated for it. NULL is a no-op. */
+int gdn_decode_graph_destroy(gdn_decode_graph* graph);
 
 /* ------------------------------------------------------------------------ */
 /* chunked prefill: variable-length sequences packed by cu_seqlens           */

@@ -192,6 +192,51 @@ def test_decode_empty_batch_is_a_no_op(lib):
     lib.gdn_state_pool_destroy(h)
 
 
+@pytest.mark.parametrize("case", ["null_pool", "zero_entries", "too_many", "bad_flags", "batch0", "no_err",
+                                  "other_err", "bad_entry", "misaligned_storage"])
+def test_decode_graph_create_argument_errors(lib, case):
+    # every case fails in the host checks, before the library touches HIP
+    buf, h = _make_pool(lib)
+    _, addr = _fake_storage()
+    _, err = _fake_storage()
+    n, flags, pool, storages = 2, 0, h, None
+    ents = [_decode_args(addr, err_flag=err), _decode_args(addr, err_flag=err)]
+    if case == "null_pool":
+        pool = None
+    elif case == "zero_entries":
+        n = 0
+    elif case == "too_many":
+        n = gdn.GDN_GRAPH_MAX_ENTRIES + 1
+    elif case == "bad_flags":
+        flags = 2
+    elif case == "batch0":
+        ents[1].batch = 0
+    elif case == "no_err":
+        ents[0].err_flag = None
+        ents[1].err_flag = None
+    elif case == "other_err":
+        ents[1].err_flag = err + 4
+    elif case == "bad_entry":
+        ents[1].dk = 32
+    elif case == "misaligned_storage":
+        storages = (c_void_p * 2)(None, addr + 4)
+    arr = (gdn.DecodeArgs * 2)(*ents)
+    out = c_void_p(1234)
+    assert lib.gdn_decode_graph_create(pool, n, arr, storages, flags, byref(out)) != gdn.GDN_OK
+    assert out.value == 1234
+    assert len(lib.gdn_last_error()) > 0
+    lib.gdn_state_pool_destroy(h)
+
+
+def test_decode_graph_null_handles(lib):
+    n, f = ctypes.c_uint32(), c_int32()
+    assert lib.gdn_decode_graph_poll(None, byref(n), byref(f)) == gdn.GDN_E_INVALID
+    assert lib.gdn_decode_graph_launch(None, None) == gdn.GDN_E_INVALID
+    assert lib.gdn_decode_graph_wait_entry(None, 0, None) == gdn.GDN_E_INVALID
+    assert lib.gdn_decode_graph_sync_entry(None, 0) == gdn.GDN_E_INVALID
+    assert lib.gdn_decode_graph_destroy(None) == gdn.GDN_OK
+
+
 def _verify_args(addr, **kw):
     a = gdn.VerifyArgs()
     a.batch, a.num_draft, a.num_k_heads, a.num_v_heads, a.dk, a.dv = 4, 3, 1, 2, 16, 16
