@@ -132,11 +132,11 @@ struct TokenScratch {
 // rows are still being read from LDS. `after_token` must be set when the
 // scratch was used by a previous token of the same workgroup (its last
 // readers are then waited for).
-template <int DK, int DV, typename T>
-__device__ __forceinline__ void token_update(const DecodeParams& p, size_t qk_off, size_t gh,
-                                             f4 (&st)[DecodeShape<DK, DV>::RPT], TokenScratch<DK, DV>& sm,
+template <int DK, int DV, int DVW, typename T>
+__device__ __forceinline__ void token_update(const DecodeParams& p, size_t qk_off, size_t gh, int c0,
+                                             f4 (&st)[DecodeShape<DK, DVW>::RPT], TokenScratch<DK, DVW>& sm,
                                              bool after_token, f4* out) {
-    using Sh = DecodeShape<DK, DV>;
+    using Sh = DecodeShape<DK, DVW>;
     constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NW = Sh::NW;
     constexpr int KPL = (DK + 63) / 64;   // q/k elements per lane
     const int tid = threadIdx.x;
@@ -169,7 +169,7 @@ __device__ __forceinline__ void token_update(const DecodeParams& p, size_t qk_of
     const float kq = skq * rk * rq;          // k^ . q~
     const float eg = expf(p.g[gh]);
     const float bt = p.beta[gh];
-    const f4 vv = Elem<T>::load4(p.v, gh * DV + 4 * cg);
+    const f4 vv = Elem<T>::load4(p.v, gh * DV + c0 + 4 * cg);
     if (after_token) __syncthreads();        // the previous token's readers of sm.k are done
     if (wave == 0) {
 #pragma unroll
@@ -220,25 +220,26 @@ __device__ __forceinline__ void token_update(const DecodeParams& p, size_t qk_of
 
     // delta correction, output, and the new tile
     const f4 u = bt * (vv - eg * A);
-    if (rg == 0) Elem<T>::store4(p.o, gh * DV + 4 * cg, eg * C + kq * u);
+    if (rg == 0) Elem<T>::store4(p.o, gh * DV + c0 + 4 * cg, eg * C + kq * u);
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int row = rg + RG * m;
         st[m] = eg * st[m] + sm.k[row] * u;
-        if (out != nullptr) __builtin_nontemporal_store(st[m], out + row * CG + cg);
+        if (out != nullptr) __builtin_nontemporal_store(st[m], out + row * (DV / 4) + c0 / 4 + cg);
     }
 }
 
 // load / store of this thread's slice of a (slot, head) tile, 128-bit
 // non-temporal (a tile is touched once per launch)
-template <int DK, int DV>
-__device__ __forceinline__ void load_tile(const DecodeParams& p, int slot, int h, f4 (&st)[DecodeShape<DK, DV>::RPT]) {
-    using Sh = DecodeShape<DK, DV>;
+template <int DK, int DV, int DVW>
+__device__ __forceinline__ void load_tile(const DecodeParams& p, int slot, int h, int c0,
+                                          f4 (&st)[DecodeShape<DK, DVW>::RPT]) {
+    using Sh = DecodeShape<DK, DVW>;
     const int cg = threadIdx.x % Sh::CG, rg = threadIdx.x / Sh::CG;
     if (slot >= 0) {
-        const f4* in = reinterpret_cast<const f4*>(p.pool + (static_cast<size_t>(slot) * p.hv + h) * (DK * DV));
+        const f4* in = reinterpret_cast<const f4*>(p.pool + (static_cast<size_t>(slot) * p.hv + h) * (DK * DV) + c0);
 #pragma unroll
-        for (int m = 0; m < Sh::RPT; ++m) st[m] = __builtin_nontemporal_load(in + (rg + Sh::RG * m) * Sh::CG + cg);
+        for (int m = 0; m < Sh::RPT; ++m) st[m] = __builtin_nontemporal_load(in + (rg + Sh::RG * m) * (DV / 4) + cg);
     } else {
 #pragma unroll
         for (int m = 0; m < Sh::RPT; ++m) st[m] = f4{0.f, 0.f, 0.f, 0.f};
@@ -250,11 +251,18 @@ __device__ __forceinline__ f4* tile_ptr(const DecodeParams& p, int slot, int h, 
     return reinterpret_cast<f4*>(p.pool + (static_cast<size_t>(slot) * p.hv + h) * elems);
 }
 
-template <int DK, int DV, typename T>
-__global__ void __launch_bounds__(decode_threads(DK, DV)) gdn_decode_kernel(DecodeParams p) {
-    __shared__ TokenScratch<DK, DV> sm;
-    const int b = blockIdx.x / p.hv;
-    const int h = blockIdx.x - b * p.hv;
+// One workgroup per (request, head, column slice): NS = DV / DVW slices of
+// DVW columns. Every column of a tile is its own dk-vector under the rule
+// (all of them see the same k^ and q~), so slices are independent; each
+// slice's workgroup redoes the small q/k normalisation.
+template <int DK, int DV, int DVW, typename T>
+__global__ void __launch_bounds__(decode_threads(DK, DVW)) gdn_decode_kernel(DecodeParams p) {
+    constexpr int NS = DV / DVW;
+    __shared__ TokenScratch<DK, DVW> sm;
+    const unsigned tile = blockIdx.x / NS;
+    const int c0 = static_cast<int>(blockIdx.x - tile * NS) * DVW;
+    const int b = tile / p.hv;
+    const int h = tile - b * p.hv;
 
     const int d = p.dst[b];
     if (d < 0) return;                       // padding row
@@ -263,21 +271,25 @@ __global__ void __launch_bounds__(decode_threads(DK, DV)) gdn_decode_kernel(Deco
         if (threadIdx.x == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
         return;
     }
-    // issue the whole source tile first; the token's small loads overlap its latency
-    f4 st[DecodeShape<DK, DV>::RPT];
-    load_tile<DK, DV>(p, s, h, st);
+    // issue the whole source slice first; the token's small loads overlap its latency
+    f4 st[DecodeShape<DK, DVW>::RPT];
+    load_tile<DK, DV, DVW>(p, s, h, c0, st);
     const size_t qk_off = (static_cast<size_t>(b) * p.hk + h / p.group) * DK;
-    token_update<DK, DV, T>(p, qk_off, static_cast<size_t>(b) * p.hv + h, st, sm, false, tile_ptr(p, d, h, DK * DV));
+    token_update<DK, DV, DVW, T>(p, qk_off, static_cast<size_t>(b) * p.hv + h, c0, st, sm, false,
+                                 tile_ptr(p, d, h, DK * DV));
 }
 
 // Speculative-decode verification: draft tokens 0 .. n-1 of request b in
-// order on the tile held in registers; the tile goes to dst[b][i] after token
-// i when that entry is >= 0. The source is read once for all of them.
-template <int DK, int DV, typename T>
-__global__ void __launch_bounds__(decode_threads(DK, DV)) gdn_verify_kernel(DecodeParams p) {
-    __shared__ TokenScratch<DK, DV> sm;
-    const int b = blockIdx.x / p.hv;
-    const int h = blockIdx.x - b * p.hv;
+// order on the slice held in registers; the slice goes to dst[b][i] after
+// token i when that entry is >= 0. The source is read once for all of them.
+template <int DK, int DV, int DVW, typename T>
+__global__ void __launch_bounds__(decode_threads(DK, DVW)) gdn_verify_kernel(DecodeParams p) {
+    constexpr int NS = DV / DVW;
+    __shared__ TokenScratch<DK, DVW> sm;
+    const unsigned tile = blockIdx.x / NS;
+    const int c0 = static_cast<int>(blockIdx.x - tile * NS) * DVW;
+    const int b = tile / p.hv;
+    const int h = tile - b * p.hv;
     const int K = p.ndraft;
     const int n = p.lens != nullptr ? p.lens[b] : K;
     if (n == 0) return;
@@ -292,22 +304,23 @@ __global__ void __launch_bounds__(decode_threads(DK, DV)) gdn_verify_kernel(Deco
         if (threadIdx.x == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
         return;
     }
-    f4 st[DecodeShape<DK, DV>::RPT];
-    load_tile<DK, DV>(p, s, h, st);
+    f4 st[DecodeShape<DK, DVW>::RPT];
+    load_tile<DK, DV, DVW>(p, s, h, c0, st);
     const int j = h / p.group;
     for (int i = 0; i < n; ++i) {
         const size_t t = static_cast<size_t>(b) * K + i;      // token row
         const int d = p.dst[t];
-        token_update<DK, DV, T>(p, (t * p.hk + j) * DK, t * p.hv + h, st, sm, i > 0,
-                                d >= 0 ? tile_ptr(p, d, h, DK * DV) : nullptr);
+        token_update<DK, DV, DVW, T>(p, (t * p.hk + j) * DK, t * p.hv + h, c0, st, sm, i > 0,
+                                     d >= 0 ? tile_ptr(p, d, h, DK * DV) : nullptr);
     }
 }
 
-template <int DK, int DV, typename T, bool VERIFY>
+template <int DK, int DV, int DVW, typename T, bool VERIFY>
 int launch_shape(const DecodeParams& p, int batch, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(batch) * static_cast<unsigned>(p.hv));
-    if (VERIFY) hipLaunchKernelGGL((gdn_verify_kernel<DK, DV, T>), grid, dim3(DecodeShape<DK, DV>::NT), 0, stream, p);
-    else hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, T>), grid, dim3(DecodeShape<DK, DV>::NT), 0, stream, p);
+    const dim3 grid(static_cast<unsigned>(batch) * static_cast<unsigned>(p.hv) * static_cast<unsigned>(DV / DVW));
+    const dim3 block(DecodeShape<DK, DVW>::NT);
+    if (VERIFY) hipLaunchKernelGGL((gdn_verify_kernel<DK, DV, DVW, T>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((gdn_decode_kernel<DK, DV, DVW, T>), grid, block, 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return gdn::fail(GDN_E_HIP, std::string(VERIFY ? "gdn_decode_verify" : "gdn_decode_step") + ": launch failed: " +
@@ -315,17 +328,43 @@ int launch_shape(const DecodeParams& p, int batch, hipStream_t stream) {
     return GDN_OK;
 }
 
+// Column slices per tile. A launch has batch * HV tiles and MI355X has 256
+// CUs; a small batch leaves most of them idle while each workgroup streams a
+// whole 64 KiB tile. Measured on MI355X at HV = 32, 128 x 128 (in-place bf16
+// decode): 4 slices are fastest up to 64 tiles (B = 1: 3.7 us against 4.6 us
+// whole), 2 slices below 512 tiles (B = 8: 5.8 against 6.9 us), whole tiles
+// from 512 up (B = 16: 9.7 against 11.5 us split in 2). A slice keeps at
+// least 32 columns so each of its rows is a whole 128-byte line: 16-column
+// slices, which share lines between workgroups, were slower at every batch.
+int decode_split(int64_t tiles, int dv) {
+    int s = 1;
+    if (tiles < 512) s = 2;
+    if (tiles <= 64) s = 4;
+    while (s > 1 && dv / s < 32) s /= 2;
+    return s;
+}
+
+template <int DK, int DV, typename T, bool VERIFY>
+int launch_split(const DecodeParams& p, int batch, int split, hipStream_t s) {
+    if constexpr (DV / 4 >= 32)
+        if (split == 4) return launch_shape<DK, DV, DV / 4, T, VERIFY>(p, batch, s);
+    if constexpr (DV / 2 >= 32)
+        if (split == 2) return launch_shape<DK, DV, DV / 2, T, VERIFY>(p, batch, s);
+    return launch_shape<DK, DV, DV, T, VERIFY>(p, batch, s);
+}
+
 template <typename T, bool VERIFY>
 int dispatch_dv(const DecodeParams& p, int batch, int dk, int dv, hipStream_t s) {
-#define GDN_DK_CASE(DK)                                                     \
-    if (dk == DK) {                                                         \
-        switch (dv) {                                                       \
-            case 16: return launch_shape<DK, 16, T, VERIFY>(p, batch, s);   \
-            case 32: return launch_shape<DK, 32, T, VERIFY>(p, batch, s);   \
-            case 64: return launch_shape<DK, 64, T, VERIFY>(p, batch, s);   \
-            case 128: return launch_shape<DK, 128, T, VERIFY>(p, batch, s); \
-            default: break;                                                 \
-        }                                                                   \
+    const int split = decode_split(static_cast<int64_t>(batch) * p.hv, dv);
+#define GDN_DK_CASE(DK)                                                             \
+    if (dk == DK) {                                                                 \
+        switch (dv) {                                                               \
+            case 16: return launch_split<DK, 16, T, VERIFY>(p, batch, split, s);    \
+            case 32: return launch_split<DK, 32, T, VERIFY>(p, batch, split, s);    \
+            case 64: return launch_split<DK, 64, T, VERIFY>(p, batch, split, s);    \
+            case 128: return launch_split<DK, 128, T, VERIFY>(p, batch, split, s);  \
+            default: break;                                                         \
+        }                                                                           \
     }
     GDN_DK_CASE(16)
     GDN_DK_CASE(32)

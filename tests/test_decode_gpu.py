@@ -116,6 +116,17 @@ def test_decode_long_memory_variants(variant):
     _run(wl, 100)
 
 
+@pytest.mark.parametrize("B", [1, 2, 4, 12, 16])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_decode_small_batches_column_slices(B, dtype):
+    """Small batches at the 16/32-head 128 x 128 shape, where the launch cuts
+    each tile into 4 (B <= 2) or 2 (B < 16) column slices; B = 16 keeps whole
+    tiles. 20 steps, every request followed by the oracle."""
+    wl = decode_workload(f"small_b{B}", seed=90 + B, B=B, HK=16, HV=32, dk=128, dv=128, dtype=dtype,
+                         num_slots=2 * B + 2, pool_sigma=0.05, steps=20, g_range=(1e-3, 0.1))
+    _run(wl, 20)
+
+
 @pytest.mark.parametrize("dk,dv", list(itertools.product([16, 32, 64, 128], repeat=2)))
 @pytest.mark.parametrize("dtype", [F32, BF16])
 def test_decode_head_shapes_and_slot_cases(dk, dv, dtype):
