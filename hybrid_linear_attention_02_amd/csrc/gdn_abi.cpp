@@ -187,9 +187,10 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     int st = check_heads(pool, a->num_k_heads, a->num_v_heads, a->dk, a->dv, fn);
     if (st != GDN_OK) return st;
     if (a->chunk_size != 64) return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: chunk_size must be 64");
-    if (a->dtype != GDN_DTYPE_BF16)
-        return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: only GDN_DTYPE_BF16 inputs are built");
-    if (!prefill_dims_supported(a->dk, a->dv))
+    const bool f32 = a->dtype == GDN_DTYPE_F32;   // token recurrence, any pool head shape
+    if (a->dtype != GDN_DTYPE_BF16 && !f32)
+        return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: dtype must be GDN_DTYPE_BF16 or GDN_DTYPE_F32");
+    if (!f32 && !prefill_dims_supported(a->dk, a->dv))
         return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: dk must be 32, 64 or 128 and dv 16, 32, 64 or 128");
     if (!std::isfinite(a->scale) || !(a->l2_eps >= 0.0f) || !std::isfinite(a->l2_eps))
         return fail(GDN_E_INVALID, "gdn_prefill_chunked: scale must be finite and l2_eps finite and >= 0");
@@ -215,7 +216,7 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
         return fail(GDN_E_INVALID, "gdn_prefill_chunked: too many chunks");
     plan->num_chunks = static_cast<int32_t>(chunks);
     // (the transition columns and the chain pass work in 64-column groups)
-    const bool can_split = a->dk >= 64 && a->dv >= 64;
+    const bool can_split = !f32 && a->dk >= 64 && a->dv >= 64;
     plan->seg_len = can_split ? choose_seg_len(a->cu_seqlens_host, n, a->num_v_heads, a->dk, a->dv) : 0;
     int64_t segs = 0;
     for (int32_t i = 0; i < n; ++i) {
@@ -233,9 +234,9 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     plan->off_seg_offsets = off;
     off = up(off + sizeof(int32_t) * static_cast<size_t>(n + 1));
     plan->off_tp = off;
-    off = up(off + 2ull * chunks * hv * 2 * 64 * 64);
+    off = up(off + (f32 ? 0 : 2ull * chunks * hv * 2 * 64 * 64));
     plan->off_sc = off;
-    off = up(off + 4ull * chunks * hv * (5 * 64));
+    off = up(off + (f32 ? 0 : 4ull * chunks * hv * (5 * 64)));
     plan->off_se = off;
     off = up(off + (split ? 4ull * segs * hv * dk * dv : 0));
     plan->off_sm = off;
@@ -273,5 +274,6 @@ extern "C" int gdn_prefill_chunked(const gdn_pool* pool, const gdn_prefill_args*
     if (workspace_bytes < plan.bytes)
         return fail(GDN_E_INVALID, "gdn_prefill_chunked: workspace too small (need " + std::to_string(plan.bytes) +
                                        " bytes)");
+    if (a->dtype == GDN_DTYPE_F32) return gdn::launch_prefill_f32(pool, a, plan, workspace, stream);
     return gdn::launch_prefill(pool, a, plan, workspace, stream);
 }

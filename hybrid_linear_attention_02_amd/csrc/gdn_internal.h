@@ -62,5 +62,8 @@ struct PrefillPlan {
 int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* plan);
 int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const PrefillPlan& plan,
                    void* workspace, void* stream);
+// float32 inputs: the per-token rule in fp32 (chunk offsets in the workspace)
+int launch_prefill_f32(const gdn_pool* pool, const gdn_prefill_args* a, const PrefillPlan& plan,
+                       void* workspace, void* stream);
 
 }  // namespace gdn

@@ -330,7 +330,9 @@ typedef struct gdn_prefill_args {
     const int32_t* cu_seqlens_host; /* [N+1] host mirror (grid sizing, checks) */
     int32_t chunk_size;           /* must be 64 */
     int32_t num_k_heads, num_v_heads, dk, dv;
-    int32_t dtype;                /* GDN_DTYPE_BF16 (fp32 prefill: GDN_E_UNSUPPORTED) */
+    int32_t dtype;                /* GDN_DTYPE_BF16: chunked form on bf16 matrix cores, dk in
+                                     {32, 64, 128}; GDN_DTYPE_F32: the token recurrence in
+                                     fp32 (any pool head shape), for fp32 accuracy */
     const void* q;                /* [T][HK][dk] device */
     const void* k;                /* [T][HK][dk] device */
     const void* v;                /* [T][HV][dv] device */

@@ -330,7 +330,7 @@ def test_prefill_workspace_size_grows_with_chunks(lib):
 
 @pytest.mark.parametrize("change,code", [
     (dict(chunk_size=32), gdn.GDN_E_UNSUPPORTED),
-    (dict(dtype=gdn.GDN_DTYPE_F32), gdn.GDN_E_UNSUPPORTED),
+    (dict(dtype=7), gdn.GDN_E_UNSUPPORTED),
     (dict(total_tokens=5), gdn.GDN_E_INVALID),
     (dict(cu_seqlens_host=None), gdn.GDN_E_INVALID),
     (dict(q=None), gdn.GDN_E_INVALID),
@@ -367,6 +367,20 @@ def test_prefill_no_sequences_is_a_no_op(lib):
     a = _prefill_args(None, cuh)
     assert lib.gdn_prefill_chunked(h, byref(a), None, 0, None) == gdn.GDN_OK
     lib.gdn_state_pool_destroy(h)
+
+
+def test_prefill_f32_accepts_every_pool_shape_and_needs_only_offsets(lib):
+    # fp32 inputs run the token recurrence: any pool head shape, and the
+    # workspace holds only the per-sequence chunk offsets
+    for dk, dv in ((16, 16), (128, 128), (32, 64)):
+        buf, h = _make_pool(lib, hv=2, dk=dk, dv=dv)
+        _, addr = _fake_storage()
+        cuh = np.asarray([0, 64, 64, 200], np.int32)
+        a = _prefill_args(addr, cuh, dk=dk, dv=dv, dtype=gdn.GDN_DTYPE_F32)
+        n = c_size_t()
+        assert lib.gdn_prefill_workspace_bytes(h, byref(a), byref(n)) == gdn.GDN_OK
+        assert n.value == 512          # [N+1] chunk offsets and [N+1] segment offsets, 256-byte blocks
+        lib.gdn_state_pool_destroy(h)
 
 
 def test_prefill_unsupported_head_dim(lib):
