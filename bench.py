@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s
 METRIC = "GDN decode state-update HBM GB/s (% peak); chunked prefill tokens/s (MFMA %)"
 
 
@@ -273,6 +274,48 @@ def bench_prefill(reps=20, warmup=3):
         "hbm_gbs_algorithmic": (T * prefill_bytes_per_token(pw.HK, pw.HV, pw.dk, pw.dv) + pw.HV * pw.dk * pw.dv * 4)
         / steady / 1e9,
     }
+
+
+def bench_prefill_f32(reps=5):
+    """Prefill with float32 inputs (the fp32 token recurrence) at 16/32 heads,
+    128 x 128: one 8192-token sequence, and 16 sequences of 800 tokens from
+    zero states. Flops: 6 dk dv per token and value head (H^T k, H^T q and
+    the rank-one update), against the fp32 vector peak."""
+    import torch
+    from hybrid_linear_attention_02_amd import gdn
+    from hybrid_linear_attention_02_amd.workloads import F32, prefill_workload
+
+    out = {}
+    for name, lengths in (("one_seq_t8192", [8192]), ("packed_16x800", [800] * 16)):
+        pw = prefill_workload(name, seed=2, lengths=lengths, HK=16, HV=32, dk=128, dv=128, dtype=F32,
+                              num_slots=2 * len(lengths))
+        tk = pw.tokens
+        d = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        q, k, v, g, b = d(tk.q), d(tk.k), d(tk.v), d(tk.g), d(tk.beta)
+        o = torch.empty_like(v)
+        pool = gdn.gdn_state_pool_create(pw.num_slots, 32, 128, 128)
+        pool.alloc(pw.num_slots)
+        N = len(lengths)
+        src = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+        dst = torch.arange(N, 2 * N, dtype=torch.int32, device="cuda")
+        cu = d(pw.cu_seqlens)
+        ws = gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src, dst)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src, dst, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e-3
+        T = int(pw.cu_seqlens[-1])
+        tflops = 6 * 128 * 128 * 32 * T / t / 1e12
+        out[name] = {"ms": round(t * 1e3, 3), "tok_per_s": round(T / t, 1),
+                     "us_per_token_step": round(t * 1e6 / max(lengths), 3),
+                     "tflops_fp32": round(tflops, 2), "frac_fp32_valu": round(tflops / FP32_VALU_PEAK_TFLOPS, 4)}
+        pool.close()
+    out["bound"] = "alu (a latency-bound chain per token; the state stays in registers)"
+    return out
 
 
 def bench_verify(reps=50, warmup=5):
@@ -694,6 +737,7 @@ def main():
     pre = None if args.no_prefill else bench_prefill()
     if pre is not None and not args.no_cpu_baseline:
         pre["cpu_baseline"] = cpu_pre
+    pre32 = None if args.no_prefill else bench_prefill_f32()
     ver = bench_verify()
     xfer = bench_transfer()
     grf = bench_graph()
@@ -721,7 +765,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(d["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(d["achieved"] / HBM_PEAK_GBS, 4), "traffic": d["traffic"],
-            "kernel": "gdn_decode_kernel<128,128,bf16>", "launch_us_mean": round(d["launch_ms_mean"] * 1e3, 2),
+            "kernel": "gdn_decode_kernel<128,128,128,bf16> (whole tiles)", "launch_us_mean": round(d["launch_ms_mean"] * 1e3, 2),
             "timing": "HIP-graph replay of the K timed steps; achieved = bytes per launch / (replay span / K)",
         },
         "eager": {k: round(v, 2) for k, v in d["eager"].items()},
@@ -733,6 +777,7 @@ def main():
         "transfer": xfer,
         "decode_graph": grf,
         "prefill": pre,
+        "prefill_f32": pre32,
     }
     print(json.dumps(line))
 
