@@ -268,7 +268,9 @@ def bench_prefill(reps=20, warmup=3):
         "timing": "value: back-to-back calls (host overlapped); graph_ms: HIP-graph replay; "
                   "latency_ms: one synchronised call including host marshalling and planning",
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": tflops / BF16_PEAK_TFLOPS,
+                     "traffic": _traffic("prefill_t8192_counters.md", ["gdn_prefill.hip", "gdn_abi.cpp"],
+                                         "hbm_bytes_per_call"),
                      "scope": "whole gdn_prefill_chunked call (prep + intra-chunk + recurrence kernels)"},
         "algorithmic_gflop": flops / 1e9,
         "hbm_gbs_algorithmic": (T * prefill_bytes_per_token(pw.HK, pw.HV, pw.dk, pw.dv) + pw.HV * pw.dk * pw.dv * 4)
