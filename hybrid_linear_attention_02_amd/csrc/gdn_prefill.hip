@@ -328,10 +328,18 @@ __device__ __forceinline__ f32x4 mm16(f32x4 x, f32x4 y, f32x4 acc) {
 template <int DK>
 __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     constexpr int KS = DK / 32;       // MFMA k-steps over dk
-    constexpr int SD = 20;            // row stride (floats) of the 16 x 16 block tiles in LDS
-    __shared__ __align__(16) float sAd[4 * 16 * SD];   // diagonal blocks of A, row-major
-    __shared__ __align__(16) float sTc[4 * 16 * SD];   // diagonal blocks of T, column-major
-    __shared__ __align__(16) float sTr[4 * 16 * SD];   // diagonal blocks of T, row-major
+    // The four 16 x 16 diagonal blocks of a 64 x 64 matrix in LDS: block b
+    // at b * BS floats, rows of 16 floats. The 16-float gap between blocks
+    // puts the four lane groups (one per block) on different banks.
+    // 9.5 KiB in all, so 16 of these one-wave workgroups fit on a CU (as many
+    // as the registers allow).
+    constexpr int SD = 16;            // row stride (floats)
+    constexpr int BS = 16 * SD + 16;  // block stride (floats)
+    // diagonal blocks of A (row-major) until the solve has read them, then
+    // of T (column-major): the workgroup is one wave, so every read of A
+    // precedes the first write of T
+    __shared__ __align__(16) float sAT[4 * BS];
+    __shared__ __align__(16) float sTr[4 * BS];        // diagonal blocks of T, row-major
     __shared__ __align__(16) float sGam[kC], sBeta[kC], sRk[kC], sRq[kC];
 
     const int c = blockIdx.x;
@@ -441,7 +449,7 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
                 a[e] = (sc < r) ? br * dec * kk[e] * rkr * rks[e] : 0.f;
                 pt[ts][e] = dec * kq[e] * rq * rks[e];
             }
-            if (ts == tr) *reinterpret_cast<f32x4*>(sAd + (16 * tr + l16) * SD + 4 * g4) = a;
+            if (ts == tr) *reinterpret_cast<f32x4*>(sAT + tr * BS + l16 * SD + 4 * g4) = a;
             else ra[tr * (tr - 1) / 2 + ts] = a;
         }
 #pragma unroll
@@ -467,7 +475,7 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float* arow = sAd + (16 * bb + r) * SD;
+            const float* arow = sAT + bb * BS + r * SD;
             float acc = (r == t) ? 1.f : 0.f;
 #pragma unroll
             for (int s4 = 0; s4 < r; s4 += 4) {
@@ -480,17 +488,17 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         }
 #pragma unroll
         for (int r4 = 0; r4 < 16; r4 += 4)
-            *reinterpret_cast<f32x4*>(sTc + (16 * bb + t) * SD + r4) = f32x4{x[r4], x[r4 + 1], x[r4 + 2], x[r4 + 3]};
+            *reinterpret_cast<f32x4*>(sAT + bb * BS + t * SD + r4) = f32x4{x[r4], x[r4 + 1], x[r4 + 2], x[r4 + 3]};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sTr[(16 * bb + r) * SD + t] = x[r];
+        for (int r = 0; r < 16; ++r) sTr[bb * BS + r * SD + t] = x[r];
     }
     lds_barrier();
     // diagonal blocks in both operand layouts: C (lane = column) and R (lane = row)
     f32x4 tc[3], trf[4];
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
-        if (bb < 3) tc[bb] = *reinterpret_cast<const f32x4*>(sTc + (16 * bb + l16) * SD + 4 * g4);
-        trf[bb] = *reinterpret_cast<const f32x4*>(sTr + (16 * bb + l16) * SD + 4 * g4);
+        if (bb < 3) tc[bb] = *reinterpret_cast<const f32x4*>(sAT + bb * BS + l16 * SD + 4 * g4);
+        trf[bb] = *reinterpret_cast<const f32x4*>(sTr + bb * BS + l16 * SD + 4 * g4);
     }
     // Off the diagonal, T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj), level by
     // level on the fp32 MFMA; blocks used again later are kept in layout C,
