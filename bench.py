@@ -278,6 +278,45 @@ def bench_prefill(reps=20, warmup=3):
     }
 
 
+def bench_prefill_packed(reps=5):
+    """Chunked prefill of the long/packed workload: one 50,000-token sequence
+    plus 16 sequences of U[1K, 16K] tokens in one call, zero initial states,
+    16/32 heads, 128 x 128 bf16. Many independent (sequence, head) chains fill
+    more of the chip than the single 8192-token sequence."""
+    import torch
+    from hybrid_linear_attention_02_amd import gdn
+    from hybrid_linear_attention_02_amd.workloads import long_packed_prefill
+
+    pw = long_packed_prefill()
+    tk = pw.tokens
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, g, b = bf(tk.q), bf(tk.k), bf(tk.v), dev(tk.g), dev(tk.beta)
+    T = int(pw.cu_seqlens[-1])
+    N = len(pw.cu_seqlens) - 1
+    o = torch.empty((T, pw.HV, pw.dv), dtype=torch.bfloat16, device="cuda")
+    pool = gdn.gdn_state_pool_create(pw.num_slots, pw.HV, pw.dk, pw.dv)
+    pool.alloc(pw.num_slots)
+    cu = dev(pw.cu_seqlens)
+    src = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+    dst = torch.arange(1, N + 1, dtype=torch.int32, device="cuda")
+    ws = gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src, dst)
+    torch.cuda.synchronize()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src, dst, workspace=ws)
+    e.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(e) / reps * 1e-3
+    tflops = T * prefill_flops_per_token(pw.HV, pw.dk, pw.dv) / t / 1e12
+    pool.close()
+    del ws, o, q, k, v
+    return {"workload": f"long_packed_prefill_bf16_{N}seqs_t{T}_hk16_hv32_128x128", "tokens": T, "ms": round(t * 1e3, 3),
+            "tok_per_s": round(T / t, 1), "tflops_algorithmic": round(tflops, 1),
+            "frac_bf16_mfma": round(tflops / BF16_PEAK_TFLOPS, 4)}
+
+
 def bench_prefill_f32(reps=5):
     """Prefill with float32 inputs (the fp32 token recurrence) at 16/32 heads,
     128 x 128: one 8192-token sequence, and 16 sequences of 800 tokens from
@@ -740,6 +779,7 @@ def main():
     if pre is not None and not args.no_cpu_baseline:
         pre["cpu_baseline"] = cpu_pre
     pre32 = None if args.no_prefill else bench_prefill_f32()
+    packed = None if args.no_prefill else bench_prefill_packed()
     ver = bench_verify()
     xfer = bench_transfer()
     grf = bench_graph()
@@ -779,6 +819,7 @@ def main():
         "transfer": xfer,
         "decode_graph": grf,
         "prefill": pre,
+        "prefill_packed": packed,
         "prefill_f32": pre32,
     }
     print(json.dumps(line))
