@@ -77,7 +77,7 @@ def _check(wl, res, o_ref, states, dst, rows, what):
 
 
 @pytest.mark.parametrize("dtype", [F32, BF16])
-@pytest.mark.parametrize("K", [1, 3, 8])
+@pytest.mark.parametrize("K", [1, 3, 8, 64])
 def test_verify_matches_oracle(dtype, K):
     B = 6
     wl = verify_workload(f"verify_{dtype}_k{K}", seed=50 + K, B=B, K=K, HK=2, HV=4, dk=32, dv=64, dtype=dtype,
