@@ -344,7 +344,7 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
 
     const int c = blockIdx.x;
     const int h = blockIdx.y;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;       // one wave: lets the compiler bound g4 below
     const int g4 = lane >> 4, l16 = lane & 15;
     if (c >= p.num_chunks) return;
     const int n = find_seq(p.chunk_off, p.n_seqs, c);
@@ -406,7 +406,7 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     for (int tt = 0; tt < 4; ++tt) {
         const float sk = row_sumsq(kr[tt]);
         const int r = 16 * tt + l16;
-        if (g4 == 0) sRk[r] = (r < len) ? 1.0f / sqrtf(sk + p.eps) : 0.f;
+        if (g4 == 0) sRk[r] = (r < len) ? __builtin_amdgcn_rsqf(sk + p.eps) : 0.f;
     }
     lds_barrier();
 
@@ -424,9 +424,9 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         for (int ks = 0; ks < KS; ++ks) qr[ks] = qn[ks];
         if (tr < 3) load_rows(p.q, tr + 1, qn);
         const int r = 16 * tr + l16;           // this lane's row
-        const float rq = (r < len) ? p.scale / sqrtf(row_sumsq(qr) + p.eps) : 0.f;
+        const float rq = (r < len) ? p.scale * __builtin_amdgcn_rsqf(row_sumsq(qr) + p.eps) : 0.f;
         if (g4 == 0) sRq[r] = rq;
-        const float gr = sGam[r], br = sBeta[r], rkr = sRk[r];
+        const float gr = sGam[r], brk = sBeta[r] * sRk[r];
         f32x4 pt[4];                           // pt[ts][e] = P[r][16 ts + 4 g + e]
 #pragma unroll
         for (int ts = 0; ts < 4; ++ts) {
@@ -442,12 +442,16 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
             const f32x4 gs = *reinterpret_cast<const f32x4*>(sGam + 16 * ts + 4 * g4);
             const f32x4 rks = *reinterpret_cast<const f32x4*>(sRk + 16 * ts + 4 * g4);
             f32x4 a;
+            // below the diagonal block every column precedes the row (the
+            // masks fold away there); gr - gs <= 0 wherever the mask keeps it
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int sc = 16 * ts + 4 * g4 + e;
-                const float dec = (sc <= r) ? exp2_hw(gr - gs[e]) : 0.f;
-                a[e] = (sc < r) ? br * dec * kk[e] * rkr * rks[e] : 0.f;
-                pt[ts][e] = dec * kq[e] * rq * rks[e];
+                float dec = exp2_hw(gr - gs[e]);
+                if (ts == tr) dec = (sc <= r) ? dec : 0.f;
+                const float dr = dec * rks[e];
+                a[e] = (ts < tr || sc < r) ? brk * dr * kk[e] : 0.f;
+                pt[ts][e] = rq * dr * kq[e];
             }
             if (ts == tr) *reinterpret_cast<f32x4*>(sAT + tr * BS + l16 * SD + 4 * g4) = a;
             else ra[tr * (tr - 1) / 2 + ts] = a;
