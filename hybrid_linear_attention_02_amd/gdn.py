@@ -348,11 +348,16 @@ class DecodeGraph:
     def __init__(self, pool: StatePool, entries, storages=None, *, layer_events: bool = False, keep=()):
         n = len(entries)
         arr = (DecodeArgs * max(n, 1))(*entries)
+        import torch
         st = None
         if storages is not None:
             if len(storages) != n:
                 raise ValueError("storages must have one entry per launch")
-            st = (c_void_p * n)(*[None if t is None else _dev(t, "storage") for t in storages])
+            want = pool.num_slots * pool.num_v_heads * pool.dk * pool.dv
+            for t in storages:
+                if t is not None and t.numel() != want:
+                    raise ValueError("every storage must hold the pool's num_slots * HV * dk * dv floats")
+            st = (c_void_p * n)(*[None if t is None else _dev(t, "storage", torch.float32) for t in storages])
         h = c_void_p()
         flags = GDN_GRAPH_LAYER_EVENTS if layer_events else 0
         _check(load_library().gdn_decode_graph_create(c_void_p(pool.handle), n, arr, st, flags, byref(h)))
