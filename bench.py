@@ -677,13 +677,17 @@ def achievable():
         return min(ts)
 
     tc = best(lambda: c.copy_(a))
+    tf = best(lambda: c.fill_(1.5))
     tg = best(lambda: torch.matmul(x, y))
     copy_gbs = 2 * n * 4 / tc / 1e9
+    fill_gbs = n * 4 / tf / 1e9
     gemm = 2 * 8192 ** 3 / tg / 1e12
     del a, c, x, y
     return {"copy_gbs": round(copy_gbs, 1), "copy_frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "fill_gbs": round(fill_gbs, 1), "fill_frac_of_peak": round(fill_gbs / HBM_PEAK_GBS, 4),
             "gemm_bf16_tflops": round(gemm, 1), "gemm_frac_of_peak": round(gemm / BF16_PEAK_TFLOPS, 4),
-            "protocol": "best of 10: 1 GiB float32 device copy; torch.matmul of two 8192x8192 bf16 matrices"}
+            "protocol": "best of 10: 1 GiB float32 device copy (bytes read + written); 1 GiB device fill "
+                        "(bytes written); torch.matmul of two 8192x8192 bf16 matrices"}
 
 
 def run_counters(launches=5, copy_mib=128):
