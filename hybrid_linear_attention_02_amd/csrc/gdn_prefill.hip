@@ -284,19 +284,61 @@ __device__ __forceinline__ void lds_barrier() {
 // prep: first chunk and first segment of every sequence
 // ---------------------------------------------------------------------------
 
-__global__ void chunk_offsets_kernel(PrefillParams p) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    int32_t acc = 0, segs = 0;
-    for (int i = 0; i < p.n_seqs; ++i) {
-        p.chunk_off_w[i] = acc;
-        p.seg_off_w[i] = segs;
-        const int32_t len = p.cu[i + 1] - p.cu[i];
-        const int32_t nc = len > 0 ? (len + kC - 1) / kC : 0;
-        acc += nc;
-        segs += (p.seg_len == 0 || nc <= p.seg_len) ? 1 : (nc + p.seg_len - 1) / p.seg_len;
+// Exclusive prefix sums of the chunk and segment counts of every sequence,
+// 1024 sequences per round: a scan inside each wave, then the wave totals
+// through LDS. (A zero-length sequence has no chunk but one segment, which
+// carries its state to the destination.)
+constexpr int kOffThreads = 1024;
+
+__global__ void __launch_bounds__(kOffThreads) chunk_offsets_kernel(PrefillParams p) {
+    constexpr int NWV = kOffThreads / 64;
+    __shared__ int32_t wc[NWV], ws[NWV];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int32_t carry_c = 0, carry_s = 0;
+    for (int base = 0; base < p.n_seqs; base += kOffThreads) {
+        const int i = base + tid;
+        int32_t nc = 0, ns = 0;
+        if (i < p.n_seqs) {
+            const int32_t len = p.cu[i + 1] - p.cu[i];
+            nc = len > 0 ? (len + kC - 1) / kC : 0;
+            ns = (p.seg_len == 0 || nc <= p.seg_len) ? 1 : (nc + p.seg_len - 1) / p.seg_len;
+        }
+        int32_t xc = nc, xs = ns;               // inclusive scan inside the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t yc = __shfl_up(xc, off), ys = __shfl_up(xs, off);
+            if (lane >= off) {
+                xc += yc;
+                xs += ys;
+            }
+        }
+        if (lane == 63) {
+            wc[w] = xc;
+            ws[w] = xs;
+        }
+        __syncthreads();
+        int32_t oc = carry_c, os = carry_s, tc = 0, ts = 0;
+#pragma unroll
+        for (int k = 0; k < NWV; ++k) {
+            if (k < w) {
+                oc += wc[k];
+                os += ws[k];
+            }
+            tc += wc[k];
+            ts += ws[k];
+        }
+        if (i < p.n_seqs) {
+            p.chunk_off_w[i] = oc + xc - nc;
+            p.seg_off_w[i] = os + xs - ns;
+        }
+        carry_c += tc;
+        carry_s += ts;
+        __syncthreads();                        // wc / ws are rewritten next round
     }
-    p.chunk_off_w[p.n_seqs] = acc;
-    p.seg_off_w[p.n_seqs] = segs;
+    if (tid == 0) {
+        p.chunk_off_w[p.n_seqs] = carry_c;
+        p.seg_off_w[p.n_seqs] = carry_s;
+    }
 }
 
 // Locate chunk c: the last sequence n with chunk_off[n] <= c.
@@ -1233,7 +1275,7 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
     p.scale = a->scale;
     p.eps = a->l2_eps;
 
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(kOffThreads), 0, s, p);
     int st = check_launch("chunk-offset");
     if (st != GDN_OK) return st;
     const int nw = a->dv >= 64 ? 4 : a->dv / 16;
