@@ -51,12 +51,17 @@ struct TokenParams {
 };
 
 // First 64-token chunk of every sequence (exclusive prefix sum of
-// ceil(len / 64)), one wavefront scanning 64 sequences at a time.
-__global__ void __launch_bounds__(64) token_chunk_offsets_kernel(TokenParams p) {
-    const int lane = threadIdx.x;
+// ceil(len / 64)), 1024 sequences per round: a scan inside each wave, then
+// the wave totals through LDS.
+constexpr int kOffThreads = 1024;
+
+__global__ void __launch_bounds__(kOffThreads) token_chunk_offsets_kernel(TokenParams p) {
+    constexpr int NWV = kOffThreads / 64;
+    __shared__ int wsum[NWV];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     int carry = 0;
-    for (int base = 0; base < p.n_seqs; base += 64) {
-        const int i = base + lane;
+    for (int base = 0; base < p.n_seqs; base += kOffThreads) {
+        const int i = base + tid;
         int nc = 0;
         if (i < p.n_seqs) nc = (p.cu[i + 1] - p.cu[i] + 63) / 64;
         int x = nc;
@@ -65,10 +70,19 @@ __global__ void __launch_bounds__(64) token_chunk_offsets_kernel(TokenParams p) 
             const int y = __shfl_up(x, off);
             if (lane >= off) x += y;
         }
-        if (i < p.n_seqs) p.chunk_off_w[i] = carry + x - nc;
-        carry += __shfl(x, 63);
+        if (lane == 63) wsum[w] = x;
+        __syncthreads();
+        int o = carry, t = 0;
+#pragma unroll
+        for (int k = 0; k < NWV; ++k) {
+            if (k < w) o += wsum[k];
+            t += wsum[k];
+        }
+        if (i < p.n_seqs) p.chunk_off_w[i] = o + x - nc;
+        carry += t;
+        __syncthreads();                        // wsum is rewritten next round
     }
-    if (lane == 0) p.chunk_off_w[p.n_seqs] = carry;
+    if (tid == 0) p.chunk_off_w[p.n_seqs] = carry;
 }
 
 constexpr int kAhead = 2;                 // tokens of inputs in flight
@@ -368,7 +382,7 @@ int launch_prefill_f32(const gdn_pool* pool, const gdn_prefill_args* a, const Pr
     p.scale = a->scale;
     p.eps = a->l2_eps;
     if (p.ckpt != nullptr) {
-        hipLaunchKernelGGL(token_chunk_offsets_kernel, dim3(1), dim3(64), 0, s, p);
+        hipLaunchKernelGGL(token_chunk_offsets_kernel, dim3(1), dim3(kOffThreads), 0, s, p);
         const int st = check("chunk-offset");
         if (st != GDN_OK) return st;
     }

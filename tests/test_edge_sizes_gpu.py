@@ -28,17 +28,22 @@ def _torch():
 @pytest.mark.parametrize("dtype", [BF16, F32])
 def test_prefill_thousands_of_tiny_sequences(dtype):
     """3000 sequences of 0-3, 63-65 or 130 tokens packed into one call, from
-    pool states or zero, with skipped entries: exercises the chunk-offset
-    scan, the chunk-to-sequence search and grids of many workgroups."""
+    pool states or zero, with skipped entries and checkpoints: exercises the
+    chunk-offset scans, the chunk-to-sequence search and grids of many
+    workgroups."""
     torch = _torch()
     rng = np.random.default_rng(71)
     N = 3000
     choices = np.array([0, 1, 2, 3, 63, 64, 65, 130])
     lengths = rng.choice(choices, size=N, p=[0.1, 0.3, 0.2, 0.2, 0.05, 0.05, 0.05, 0.05])
-    NS = 2 * N + 8
+    nchunks = int(np.sum((lengths + 63) // 64))
+    NS = 8 + N + nchunks
     src = np.where(rng.random(N) < 0.5, rng.integers(0, 8, size=N), -1).astype(np.int32)
     dst = (8 + np.arange(N)).astype(np.int32)
     dst[rng.random(N) < 0.05] = -1
+    # checkpoints after a fifth of the chunks, each to its own slot (the
+    # chunk offsets then come from the multi-round scan)
+    ckpt = np.where(rng.random(nchunks) < 0.2, 8 + N + np.arange(nchunks), -1).astype(np.int32)
     pw = prefill_workload(f"tiny_many_{dtype}", seed=72, lengths=lengths.tolist(), HK=1, HV=2, dk=32, dv=32,
                           dtype=dtype, num_slots=NS, pool_sigma=0.1, src=src)
     tk = pw.tokens
@@ -52,10 +57,12 @@ def test_prefill_thousands_of_tiny_sequences(dtype):
     cu = torch.from_numpy(pw.cu_seqlens).cuda()
     gdn.gdn_prefill_chunked(pool, q, k, v, to_dev(tk.g, "f32"), to_dev(tk.beta, "f32"), o, cu, pw.cu_seqlens,
                             torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda(), scale=32 ** -0.5,
-                            l2_eps=EPS)
+                            l2_eps=EPS, ckpt_slots=torch.from_numpy(ckpt).cuda())
     torch.cuda.synchronize()
+    states = {}
     o_ref, _, fin = oracle_prefill(pw.pool, pw.cu_seqlens, src, dst, as_f64(tk.q, dtype), as_f64(tk.k, dtype),
-                                   as_f64(tk.v, dtype), tk.g, tk.beta, 32 ** -0.5, EPS)
+                                   as_f64(tk.v, dtype), tk.g, tk.beta, 32 ** -0.5, EPS, ckpt=ckpt,
+                                   ckpt_states=states)
     og = out_f64(o)
     got = storage.cpu().numpy()
     cuh = pw.cu_seqlens
@@ -68,7 +75,11 @@ def test_prefill_thousands_of_tiny_sequences(dtype):
     for n in range(N):
         if dst[n] >= 0:
             check_state(got[dst[n]], fin[n], dtype, f"seq {n} slot {dst[n]}")
-    untouched = np.setdiff1d(np.arange(NS), dst[dst >= 0])
+    assert len(states) > 100
+    for c, h in states.items():
+        check_state(got[ckpt[c]], h, dtype, f"checkpoint {c} slot {ckpt[c]}")
+    written = set(dst[dst >= 0].tolist()) | {int(ckpt[c]) for c in states}
+    untouched = np.array(sorted(set(range(NS)) - written))
     np.testing.assert_array_equal(got[untouched], pw.pool[untouched])
     pool.close()
 
