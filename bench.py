@@ -445,7 +445,8 @@ def bench_graph(reps=200, warmup=20):
     structs ("eager"), and replayed as one recorded graph. Rates are wall-clock
     over `reps` back-to-back steps, host launch cost included.
       tiny_chain: the tiny fp32 workload's 8 sequential tokens (1 request,
-        2 value heads, 16 x 16), slot 1 -> 2 then in place;
+        2 value heads, 16 x 16), slot 1 -> 2 then in place; also as one
+        verify launch over the 8 known tokens (Python binding call included);
       stack_b{B}: one token through 32 GDN layers (own storages, in place) at
         16/32 heads, 128 x 128 bf16, for B = 1 and 8 requests."""
     import ctypes
@@ -528,9 +529,27 @@ def bench_graph(reps=200, warmup=20):
         entries.append((q, k, v, dev(tk.g, None), dev(tk.beta, None), torch.empty_like(v),
                         t1 if i == 0 else t22, t2 if i == 0 else t22))
     r = run(pool, entries, None)
+    # the same 8 known tokens as one verify launch (slot 1 -> the state after
+    # every token kept in slot 2, i.e. in place after the first): the chain
+    # then runs inside one kernel with the state in registers
+    cat = lambda i: torch.stack([e[i][0] for e in entries])[None]
+    vq, vk, vv, vg, vb = (cat(i) for i in range(5))
+    vo = torch.empty_like(vv)
+    vsrc = torch.tensor([1], dtype=torch.int32, device="cuda")
+    vdst = torch.tensor([[-1] * 7 + [2]], dtype=torch.int32, device="cuda")
+    fused = lambda: gdn.gdn_decode_verify(pool, vq, vk, vv, vg, vb, vo, vsrc, vdst)
+    for _ in range(warmup):
+        fused()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fused()
+    torch.cuda.synchronize()
+    t_fused = (time.perf_counter() - t0) / reps
     res["tiny_chain_8_tokens"] = {"binding_us_per_token": r["binding"] / 8 * 1e6,
                                   "eager_us_per_token": r["eager"] / 8 * 1e6,
                                   "graph_us_per_token": r["graph"] / 8 * 1e6,
+                                  "one_verify_launch_us_per_token": t_fused / 8 * 1e6,
                                   "speedup": r["eager"] / r["graph"],
                                   "speedup_vs_binding": r["binding"] / r["graph"]}
     pool.close()
