@@ -135,7 +135,9 @@ static bool prefill_dims_supported(int32_t dk, int32_t dv) {
 // resident per CU), each round as many steps as its longest chain. Costs per
 // step are measured cycle counts of the MI355X kernels: state pass 2800 (per
 // chunk), output pass 3800 (per chunk, one extra step), chain pass 9700 (per
-// segment hop). Returns 0 (no split) when one pass is estimated fastest.
+// segment hop with a transition product; the first segment runs from the true
+// initial state in the state pass, value columns only, and its hop is a copy
+// costed at a third). Returns 0 (no split) when one pass is estimated fastest.
 int32_t choose_seg_len(const int32_t* cu, int32_t n, int32_t hv, int32_t dk, int32_t dv) {
     constexpr double kState = 2800, kOut = 3800, kHop = 9700;
     const int64_t w_out = static_cast<int64_t>(hv) * (dv / 64);          // workgroups per segment, output pass
@@ -153,13 +155,13 @@ int32_t choose_seg_len(const int32_t* cu, int32_t n, int32_t hv, int32_t dk, int
             const int64_t nseg = (L == 0 || c <= L) ? 1 : (c + L - 1) / L;
             const int64_t seg = (nseg == 1) ? c : L;
             out_steps += (c + nseg) * w_out;
-            if (nseg > 1) state_steps += (nseg - 1) * L * w_state;
+            if (nseg > 1) state_steps += L * w_out + (nseg - 2) * L * w_state;
             longest = std::max(longest, seg + 1);
             hops = std::max(hops, nseg - 1);
         }
         if (longest == 0) return 0.0;
         double t = kOut * pass(out_steps, longest);
-        if (hops > 0) t += kState * pass(state_steps, L) + kHop * static_cast<double>(hops);
+        if (hops > 0) t += kState * pass(state_steps, L) + kHop * (static_cast<double>(hops - 1) + 1.0 / 3.0);
         return t;
     };
     // candidates: the longest sequence cut into k equal segments, k = 2 .. 32

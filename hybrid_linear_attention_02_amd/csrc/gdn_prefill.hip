@@ -396,11 +396,11 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     if (len <= 0 || tend > p.total_tokens || p.dst[n] < 0) return;
     const int j = h / p.group;
 
-    // raw k rows as row operands in natural feature order (a contraction
-    // over dk may order its k slots freely, as long as both operands agree):
-    // kr[tt][ks] = K[16 tt + l16][32 ks + 8 g .. +7]
-    // (q rows are loaded one 16-row tile ahead below, to keep the register
-    // footprint in check)
+    // raw k and q rows as row operands in natural feature order (a
+    // contraction over dk may order its k slots freely, as long as both
+    // operands agree): kr[tt][ks] = K[16 tt + l16][32 ks + 8 g .. +7]. All
+    // of them are requested before any is used, so the wave waits for one
+    // global round trip, not five.
     const auto load_rows = [&](const uint16_t* x, int tt, u32x4* dst) {
         const int r = 16 * tt + l16;
         const size_t base = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + 8 * g4;
@@ -422,10 +422,11 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         acc += __shfl_xor(acc, 32);
         return acc;
     };
-    u32x4 kr[4][KS], qn[KS];
+    u32x4 kr[4][KS], qa[4][KS];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) load_rows(p.k, tt, kr[tt]);
-    load_rows(p.q, 0, qn);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) load_rows(p.q, tt, qa[tt]);
     // per-token g, beta; cumulative log-decay by an inclusive lane scan
     float gl = 0.f, bl = 0.f;
     if (lane < len) {
@@ -461,10 +462,7 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     f32x4 ra[6];                               // A blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 #pragma unroll
     for (int tr = 0; tr < 4; ++tr) {
-        u32x4 qr[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qr[ks] = qn[ks];
-        if (tr < 3) load_rows(p.q, tr + 1, qn);
+        const u32x4* qr = qa[tr];
         const int r = 16 * tr + l16;           // this lane's row
         const float rq = (r < len) ? p.scale * __builtin_amdgcn_rsqf(row_sumsq(qr) + p.eps) : 0.f;
         if (g4 == 0) sRq[r] = rq;
@@ -676,7 +674,8 @@ enum : int {
     kModeOutput = 0,   // outputs o, state from the slot / zero / segment initial state, final state to the slot
     kModeState = 1,    // split pass 1: no outputs; columns [0, dv) carry the state from zero with V,
                        // columns [dv, dv + dk) carry the identity with V = 0 (the transition M);
-                       // results to the segment buffers
+                       // results to the segment buffers. The first segment instead carries the
+                       // true initial state (no transition), so its result is the next start.
 };
 
 // Registers a helper wave loads one step ahead for its output rows.
@@ -729,6 +728,9 @@ prefill_recurrent_kernel(PrefillParams p) {
     // state pass, groups past dv carry columns of the transition instead
     const int ncg = p.dv / NV;
     const bool m_cols = !OUT && grp >= ncg;
+    // The first segment of a split sequence starts from the true initial
+    // state (source slot or zero), so its end state needs no transition.
+    if (m_cols && sg.first) return;
     const int vcol0 = (m_cols ? grp - ncg : grp) * NV;
     const int nch = c1 - c0;
 
@@ -899,9 +901,12 @@ prefill_recurrent_kernel(PrefillParams p) {
         if (OUT) {
             // A split sequence starts every segment, the first included, from
             // the chained initial states: the source slot is then read only by
-            // the chain pass, before the last segment may overwrite it in place.
+            // the passes before this one, before the last segment may
+            // overwrite it in place.
             if (sg.split) init = p.sh + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
             else if (ssl >= 0) init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+        } else if (sg.first && ssl >= 0) {
+            init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
         }
         if (init != nullptr) {
 #pragma unroll
@@ -1096,10 +1101,12 @@ prefill_recurrent_kernel(PrefillParams p) {
 // ---------------------------------------------------------------------------
 // split pass 2: chain the segments of each split sequence,
 // H_{s+1} = M_s H_s + E_s, one workgroup per (sequence, value head, 64 value
-// columns), one wave per 16 columns. Writes every segment's initial state
-// (the first one copied from the source slot or zero). The products are bf16
-// MFMAs on high/low splits of both factors (M_hi H_hi + M_hi H_lo + M_lo H_hi),
-// which keeps about 16 bits of the fp32 state.
+// columns), one wave per 16 columns. Writes every segment's initial state:
+// the first one copied from the source slot or zero, the second one equal to
+// the first segment's end state (that segment ran from the true initial
+// state), the rest by the product. The products are bf16 MFMAs on high/low
+// splits of both factors (M_hi H_hi + M_hi H_lo + M_lo H_hi), which keeps
+// about 16 bits of the fp32 state.
 // ---------------------------------------------------------------------------
 
 template <int DK>
@@ -1135,7 +1142,19 @@ __global__ void __launch_bounds__(256) segment_chain_kernel(PrefillParams p) {
 #pragma unroll
         for (int mu = 0; mu < MT; ++mu) H[mu] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int g = g0;; ++g) {
+    {
+        float* sh = p.sh + (static_cast<size_t>(g0) * p.hv + h) * tile;
+        const float* se = p.se + (static_cast<size_t>(g0) * p.hv + h) * tile;
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const size_t e = static_cast<size_t>(16 * mu + 4 * g4 + i) * p.dv + col;
+                sh[e] = H[mu][i];
+                H[mu][i] = se[e];
+            }
+    }
+    for (int g = g0 + 1;; ++g) {
         float* sh = p.sh + (static_cast<size_t>(g) * p.hv + h) * tile;
 #pragma unroll
         for (int mu = 0; mu < MT; ++mu)
