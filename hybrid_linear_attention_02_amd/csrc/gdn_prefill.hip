@@ -1018,18 +1018,28 @@ prefill_recurrent_kernel(PrefillParams p) {
     if (helper) {
         if (steps == 0) return;
         HelperRows<KS> rows0, rows1 = {};   // rows1 feeds the first step's discarded outputs
+        // In the state pass the helpers only stage, so their registers run a
+        // step ahead of LDS: a step stages the chunk whose loads the previous
+        // step issued, then issues the next chunk's loads, which then have a
+        // whole step to arrive (the workspace rows often come from HBM). In
+        // the output pass the emission between the loads and the staging
+        // covers their latency.
         fetch(c0);
         stage(0);
+        if (!OUT) fetch(min(c0 + 1, c1 - 1));
         lds_barrier();
         u32x4 ov[OPL];
         auto hstep = [&](int s, int b, HelperRows<KS>& cur, HelperRows<KS>& nxt) {
-            fetch(min(c0 + s + 1, c1 - 1));
             if (OUT) {
+                fetch(min(c0 + s + 1, c1 - 1));
                 fetch_rows(min(c0 + s, c1 - 1), nxt);
                 emit_rows(b ^ 1, cur, ov);
+                stage(b ^ 1);         // past the last chunk: a harmless copy into an unused buffer
+                store_rows(c0 + max(s - 1, 0), s >= 1, ov);
+            } else {
+                stage(b ^ 1);
+                fetch(min(c0 + s + 2, c1 - 1));
             }
-            stage(b ^ 1);             // past the last chunk: a harmless copy into an unused buffer
-            if (OUT) store_rows(c0 + max(s - 1, 0), s >= 1, ov);
             lds_barrier();
         };
         for (int s = 0; s < steps; s += 2) {
