@@ -67,6 +67,8 @@ enum : int {
     kScE = 4,     // exp(gamma_last)              (every entry)
 };
 
+constexpr int kInlineSeqs = 32;
+
 struct PrefillParams {
     const int32_t* cu;          // [N+1] device
     const int32_t* chunk_off;   // [N+1] device (workspace): first chunk of each sequence
@@ -101,7 +103,59 @@ struct PrefillParams {
     int32_t num_slots;
     float scale;
     float eps;
+    // For calls of at most kInlineSeqs sequences the host fills both offset
+    // tables here (the kernel arguments) and the prep kernel is not launched;
+    // inl_n is then n_seqs, else 0.
+    int32_t inl_n;
+    int32_t inl_chunk[kInlineSeqs + 1];
+    int32_t inl_seg[kInlineSeqs + 1];
 };
+
+// Chunk range [c0, c1) and segment range [s0, s1) of sequence n.
+struct SeqSpan {
+    int n, c0, c1, s0, s1;
+};
+
+// The span of the sequence holding chunk `key` (BY_SEG false) or segment
+// `key` (BY_SEG true): the last sequence whose first chunk (segment) is
+// <= key. `key` is wave-uniform. The kernel-argument tables are only ever
+// indexed by constants (a fully unrolled scan), so they stay in the argument
+// segment instead of being copied to private memory.
+template <bool BY_SEG>
+__device__ __forceinline__ SeqSpan find_span(const PrefillParams& p, int key) {
+    SeqSpan r;
+    if (p.inl_n > 0) {
+        r = SeqSpan{0, p.inl_chunk[0], p.inl_chunk[1], p.inl_seg[0], p.inl_seg[1]};
+        if (p.inl_n == 1) return r;
+#pragma unroll
+        for (int i = 1; i < kInlineSeqs; ++i) {
+            if (i < p.inl_n && (BY_SEG ? p.inl_seg[i] : p.inl_chunk[i]) <= key)
+                r = SeqSpan{i, p.inl_chunk[i], p.inl_chunk[i + 1], p.inl_seg[i], p.inl_seg[i + 1]};
+        }
+        return r;
+    }
+    const int32_t* off = BY_SEG ? p.seg_off : p.chunk_off;
+    int lo = 0, hi = p.n_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= key) lo = mid;
+        else hi = mid - 1;
+    }
+    return SeqSpan{lo, p.chunk_off[lo], p.chunk_off[lo + 1], p.seg_off[lo], p.seg_off[lo + 1]};
+}
+
+// The span of sequence n (wave-uniform).
+__device__ __forceinline__ SeqSpan span_of(const PrefillParams& p, int n) {
+    if (p.inl_n > 0) {
+        SeqSpan r{0, p.inl_chunk[0], p.inl_chunk[1], p.inl_seg[0], p.inl_seg[1]};
+        if (p.inl_n == 1) return r;
+#pragma unroll
+        for (int i = 1; i < kInlineSeqs; ++i)
+            if (i == n) r = SeqSpan{i, p.inl_chunk[i], p.inl_chunk[i + 1], p.inl_seg[i], p.inl_seg[i + 1]};
+        return r;
+    }
+    return SeqSpan{n, p.chunk_off[n], p.chunk_off[n + 1], p.seg_off[n], p.seg_off[n + 1]};
+}
 
 // Uniform base pointer plus a 32-bit per-lane byte offset: lets the compiler
 // use the scalar-base global access form (no 64-bit address per lane).
@@ -341,19 +395,10 @@ __global__ void __launch_bounds__(kOffThreads) chunk_offsets_kernel(PrefillParam
     }
 }
 
-// Locate chunk c: the last sequence n with chunk_off[n] <= c.
-__device__ __forceinline__ int find_seq(const int32_t* off, int n_seqs, int c) {
-    int lo = 0, hi = n_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= c) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
 
 // ---------------------------------------------------------------------------
-// intra-chunk: one wave per (chunk, value head)
+// intra-chunk: one wave per (chunk, key head), for every value head of the
+// key head's group
 // ---------------------------------------------------------------------------
 
 // fp32 16 x 16 x 16 product on the fp32 MFMA: acc += X Y, with X given with
@@ -373,8 +418,6 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     // The four 16 x 16 diagonal blocks of a 64 x 64 matrix in LDS: block b
     // at b * BS floats, rows of 16 floats. The 16-float gap between blocks
     // puts the four lane groups (one per block) on different banks.
-    // 9.5 KiB in all, so 16 of these one-wave workgroups fit on a CU (as many
-    // as the registers allow).
     constexpr int SD = 16;            // row stride (floats)
     constexpr int BS = 16 * SD + 16;  // block stride (floats)
     // diagonal blocks of A (row-major) until the solve has read them, then
@@ -385,16 +428,16 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     __shared__ __align__(16) float sGam[kC], sBeta[kC], sRk[kC], sRq[kC];
 
     const int c = blockIdx.x;
-    const int h = blockIdx.y;
+    const int j = blockIdx.y;                // key head
     const int lane = threadIdx.x & 63;       // one wave: lets the compiler bound g4 below
     const int g4 = lane >> 4, l16 = lane & 15;
     if (c >= p.num_chunks) return;
-    const int n = find_seq(p.chunk_off, p.n_seqs, c);
-    const int t0 = p.cu[n] + (c - p.chunk_off[n]) * kC;
+    const SeqSpan sp = find_span<false>(p, c);
+    const int n = sp.n;
+    const int t0 = p.cu[n] + (c - sp.c0) * kC;
     const int tend = p.cu[n + 1];
     const int len = min(kC, tend - t0);
     if (len <= 0 || tend > p.total_tokens || p.dst[n] < 0) return;
-    const int j = h / p.group;
 
     // raw k and q rows as row operands in natural feature order (a
     // contraction over dk may order its k slots freely, as long as both
@@ -427,154 +470,183 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     for (int tt = 0; tt < 4; ++tt) load_rows(p.k, tt, kr[tt]);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) load_rows(p.q, tt, qa[tt]);
-    // per-token g, beta; cumulative log-decay by an inclusive lane scan
-    float gl = 0.f, bl = 0.f;
-    if (lane < len) {
-        const size_t gi = static_cast<size_t>(t0 + lane) * p.hv + h;
-        gl = p.g[gi];
-        bl = p.beta[gi];
-    }
-    // in base 2 (gamma log2(e)), so every decay factor is one hardware exp2
-    float gam = gl * 1.4426950408889634f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float t = __shfl_up(gam, off);
-        if (lane >= off) gam += t;
-    }
-    const float gam_last = __shfl(gam, 63);   // padded tokens add g = 0
-    sGam[lane] = gam;
-    sBeta[lane] = bl;
-    // L2 norms of the k rows (fp32 sums of exact bf16 squares)
+    // per-token g, beta of value head h (token = lane)
+    const auto load_gb = [&](int h, float& gl, float& bl) {
+        gl = 0.f;
+        bl = 0.f;
+        if (lane < len) {
+            const size_t gi = static_cast<size_t>(t0 + lane) * p.hv + h;
+            gl = p.g[gi];
+            bl = p.beta[gi];
+        }
+    };
+    float gl_next, bl_next;
+    load_gb(j * p.group, gl_next, bl_next);
+
+    // Shared by the group's value heads: the L2 norms of the k and q rows
+    // (fp32 sums of exact bf16 squares) and the raw Gram tiles on MFMA with
+    // one row per lane (each product takes the column tile's k rows as its
+    // first operand): gkk[tr][ts] = K_ts K_tr^T, gkq = K_ts Q_tr^T, ts <= tr,
+    // packed as index tr (tr + 1) / 2 + ts.
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         const float sk = row_sumsq(kr[tt]);
         const int r = 16 * tt + l16;
         if (g4 == 0) sRk[r] = (r < len) ? __builtin_amdgcn_rsqf(sk + p.eps) : 0.f;
     }
-    lds_barrier();
-
-    // Gram tiles on MFMA with one row per lane (each product takes the
-    // column tile's k rows as its first operand): A (strictly lower), kept in
-    // registers off the diagonal and in LDS on it, and P, which goes to the
-    // workspace as row-operand fragments. The q rows of tile tr also give
-    // their norms.
-    u32x4* Pf = reinterpret_cast<u32x4*>(p.tp + ((static_cast<size_t>(c) * p.hv + h) * 2 + 1) * (kC * kC));
-    f32x4 ra[6];                               // A blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    float rqv[4];
 #pragma unroll
     for (int tr = 0; tr < 4; ++tr) {
-        const u32x4* qr = qa[tr];
-        const int r = 16 * tr + l16;           // this lane's row
-        const float rq = (r < len) ? p.scale * __builtin_amdgcn_rsqf(row_sumsq(qr) + p.eps) : 0.f;
-        if (g4 == 0) sRq[r] = rq;
-        const float gr = sGam[r], brk = sBeta[r] * sRk[r];
-        f32x4 pt[4];                           // pt[ts][e] = P[r][16 ts + 4 g + e]
+        const int r = 16 * tr + l16;
+        rqv[tr] = (r < len) ? p.scale * __builtin_amdgcn_rsqf(row_sumsq(qa[tr]) + p.eps) : 0.f;
+        if (g4 == 0) sRq[r] = rqv[tr];
+    }
+    f32x4 gkk[10], gkq[10];
 #pragma unroll
-        for (int ts = 0; ts < 4; ++ts) {
-            pt[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (ts > tr) continue;
+    for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+        for (int ts = 0; ts <= tr; ++ts) {
             f32x4 kk = f32x4{0.f, 0.f, 0.f, 0.f}, kq = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const bf16x8 bk = as_bf16x8(kr[ts][ks]);
                 kk = mfma16(bk, as_bf16x8(kr[tr][ks]), kk);
-                kq = mfma16(bk, as_bf16x8(qr[ks]), kq);
+                kq = mfma16(bk, as_bf16x8(qa[tr][ks]), kq);
             }
-            const f32x4 gs = *reinterpret_cast<const f32x4*>(sGam + 16 * ts + 4 * g4);
-            const f32x4 rks = *reinterpret_cast<const f32x4*>(sRk + 16 * ts + 4 * g4);
-            f32x4 a;
-            // below the diagonal block every column precedes the row (the
-            // masks fold away there); gr - gs <= 0 wherever the mask keeps it
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int sc = 16 * ts + 4 * g4 + e;
-                float dec = exp2_hw(gr - gs[e]);
-                if (ts == tr) dec = (sc <= r) ? dec : 0.f;
-                const float dr = dec * rks[e];
-                a[e] = (ts < tr || sc < r) ? brk * dr * kk[e] : 0.f;
-                pt[ts][e] = rq * dr * kq[e];
-            }
-            if (ts == tr) *reinterpret_cast<f32x4*>(sAT + tr * BS + l16 * SD + 4 * g4) = a;
-            else ra[tr * (tr - 1) / 2 + ts] = a;
+            gkk[tr * (tr + 1) / 2 + ts] = kk;
+            gkq[tr * (tr + 1) / 2 + ts] = kq;
         }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) Pf[(tr * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(pt[2 * ks], pt[2 * ks + 1]));
-    }
-    lds_barrier();
-    {
-        const float rk = sRk[lane], rq = sRq[lane];
-        const float eg = exp2_hw(gam);
-        float* scp = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScRows * kC);
-        scp[kScX * kC + lane] = eg * rk;
-        scp[kScBeta * kC + lane] = bl;
-        scp[kScZ * kC + lane] = eg * rq;
-        scp[kScD * kC + lane] = rk * exp2_hw(gam_last - gam);
-        scp[kScE * kC + lane] = exp2_hw(gam_last);
-    }
 
-    // T = (I + A)^-1, blocked by 16. The four diagonal blocks
-    // T_bb = (I + A_bb)^-1 are solved at once, lane group b taking block b,
-    // lane t of it column t, by forward substitution over the block's rows.
-    {
-        const int bb = g4, t = l16;
-        float x[16];
+    for (int hig = 0; hig < p.group; ++hig) {
+        const int h = j * p.group + hig;
+        const float gl = gl_next, bl = bl_next;
+        if (hig + 1 < p.group) load_gb(h + 1, gl_next, bl_next);
+        // cumulative log-decay by an inclusive lane scan, in base 2
+        // (gamma log2(e)), so every decay factor is one hardware exp2
+        float gam = gl * 1.4426950408889634f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float* arow = sAT + bb * BS + r * SD;
-            float acc = (r == t) ? 1.f : 0.f;
-#pragma unroll
-            for (int s4 = 0; s4 < r; s4 += 4) {
-                const f32x4 av = *reinterpret_cast<const f32x4*>(arow + s4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (s4 + e < r) acc -= av[e] * x[s4 + e];
-            }
-            x[r] = acc;
+        for (int off = 1; off < 64; off <<= 1) {
+            const float t = __shfl_up(gam, off);
+            if (lane >= off) gam += t;
         }
-#pragma unroll
-        for (int r4 = 0; r4 < 16; r4 += 4)
-            *reinterpret_cast<f32x4*>(sAT + bb * BS + t * SD + r4) = f32x4{x[r4], x[r4 + 1], x[r4 + 2], x[r4 + 3]};
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sTr[bb * BS + r * SD + t] = x[r];
-    }
-    lds_barrier();
-    // diagonal blocks in both operand layouts: C (lane = column) and R (lane = row)
-    f32x4 tc[3], trf[4];
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-        if (bb < 3) tc[bb] = *reinterpret_cast<const f32x4*>(sAT + bb * BS + l16 * SD + 4 * g4);
-        trf[bb] = *reinterpret_cast<const f32x4*>(sTr + bb * BS + l16 * SD + 4 * g4);
-    }
-    // Off the diagonal, T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj), level by
-    // level on the fp32 MFMA; blocks used again later are kept in layout C,
-    // every block is produced in layout R for the output.
-    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 S;
-    S = mm16(ra[0], tc[0], z);                                    // A10 T00
-    const f32x4 t10c = -mm16(trf[1], S, z), t10r = -mm16(S, trf[1], z);
-    S = mm16(ra[2], tc[1], z);                                    // A21 T11
-    const f32x4 t21c = -mm16(trf[2], S, z), t21r = -mm16(S, trf[2], z);
-    S = mm16(ra[5], tc[2], z);                                    // A32 T22
-    const f32x4 t32r = -mm16(S, trf[3], z);
-    S = mm16(ra[2], t10c, mm16(ra[1], tc[0], z));                 // A20 T00 + A21 T10
-    const f32x4 t20c = -mm16(trf[2], S, z), t20r = -mm16(S, trf[2], z);
-    S = mm16(ra[5], t21c, mm16(ra[4], tc[1], z));                 // A31 T11 + A32 T21
-    const f32x4 t31r = -mm16(S, trf[3], z);
-    S = mm16(ra[5], t20c, mm16(ra[4], t10c, mm16(ra[3], tc[0], z)));   // A30 T00 + A31 T10 + A32 T20
-    const f32x4 t30r = -mm16(S, trf[3], z);
+        const float gam_last = __shfl(gam, 63);   // padded tokens add g = 0
+        lds_barrier();                          // the previous head's LDS reads are done
+        sGam[lane] = gam;
+        sBeta[lane] = bl;
+        lds_barrier();
 
-    // T to the workspace as row-operand fragments (tau, ks) = rows 16 tau ..,
-    // k block 32 ks: blocks (tau, 2 ks) and (tau, 2 ks + 1); the two all-zero
-    // fragments (0, 1) and (1, 1) are not written
-    u32x4* Tf = reinterpret_cast<u32x4*>(p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC));
-    auto put = [&](int tau, int ks, f32x4 lo, f32x4 hi) {
-        Tf[(tau * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(lo, hi));
-    };
-    put(0, 0, trf[0], z);
-    put(1, 0, t10r, trf[1]);
-    put(2, 0, t20r, t21r);
-    put(2, 1, trf[2], z);
-    put(3, 0, t30r, t31r);
-    put(3, 1, t32r, trf[3]);
+        // A (strictly lower), kept in registers off the diagonal and in LDS
+        // on it, and P, which goes to the workspace as row-operand fragments
+        u32x4* Pf = reinterpret_cast<u32x4*>(p.tp + ((static_cast<size_t>(c) * p.hv + h) * 2 + 1) * (kC * kC));
+        f32x4 ra[6];                           // A blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr) {
+            const int r = 16 * tr + l16;       // this lane's row
+            const float rq = rqv[tr];
+            const float gr = sGam[r], brk = sBeta[r] * sRk[r];
+            f32x4 pt[4];                       // pt[ts][e] = P[r][16 ts + 4 g + e]
+#pragma unroll
+            for (int ts = 0; ts < 4; ++ts) {
+                pt[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (ts > tr) continue;
+                const f32x4 kk = gkk[tr * (tr + 1) / 2 + ts], kq = gkq[tr * (tr + 1) / 2 + ts];
+                const f32x4 gs = *reinterpret_cast<const f32x4*>(sGam + 16 * ts + 4 * g4);
+                const f32x4 rks = *reinterpret_cast<const f32x4*>(sRk + 16 * ts + 4 * g4);
+                f32x4 a;
+                // below the diagonal block every column precedes the row (the
+                // masks fold away there); gr - gs <= 0 wherever the mask keeps it
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int sc = 16 * ts + 4 * g4 + e;
+                    float dec = exp2_hw(gr - gs[e]);
+                    if (ts == tr) dec = (sc <= r) ? dec : 0.f;
+                    const float dr = dec * rks[e];
+                    a[e] = (ts < tr || sc < r) ? brk * dr * kk[e] : 0.f;
+                    pt[ts][e] = rq * dr * kq[e];
+                }
+                if (ts == tr) *reinterpret_cast<f32x4*>(sAT + tr * BS + l16 * SD + 4 * g4) = a;
+                else ra[tr * (tr - 1) / 2 + ts] = a;
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) Pf[(tr * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(pt[2 * ks], pt[2 * ks + 1]));
+        }
+        lds_barrier();
+        {
+            const float rk = sRk[lane], rq = sRq[lane];
+            const float eg = exp2_hw(gam);
+            float* scp = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScRows * kC);
+            scp[kScX * kC + lane] = eg * rk;
+            scp[kScBeta * kC + lane] = bl;
+            scp[kScZ * kC + lane] = eg * rq;
+            scp[kScD * kC + lane] = rk * exp2_hw(gam_last - gam);
+            scp[kScE * kC + lane] = exp2_hw(gam_last);
+        }
+
+        // T = (I + A)^-1, blocked by 16. The four diagonal blocks
+        // T_bb = (I + A_bb)^-1 are solved at once, lane group b taking block b,
+        // lane t of it column t, by forward substitution over the block's rows.
+        {
+            const int bb = g4, t = l16;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float* arow = sAT + bb * BS + r * SD;
+                float acc = (r == t) ? 1.f : 0.f;
+#pragma unroll
+                for (int s4 = 0; s4 < r; s4 += 4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4*>(arow + s4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (s4 + e < r) acc -= av[e] * x[s4 + e];
+                }
+                x[r] = acc;
+            }
+#pragma unroll
+            for (int r4 = 0; r4 < 16; r4 += 4)
+                *reinterpret_cast<f32x4*>(sAT + bb * BS + t * SD + r4) = f32x4{x[r4], x[r4 + 1], x[r4 + 2], x[r4 + 3]};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sTr[bb * BS + r * SD + t] = x[r];
+        }
+        lds_barrier();
+        // diagonal blocks in both operand layouts: C (lane = column) and R (lane = row)
+        f32x4 tc[3], trf[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            if (bb < 3) tc[bb] = *reinterpret_cast<const f32x4*>(sAT + bb * BS + l16 * SD + 4 * g4);
+            trf[bb] = *reinterpret_cast<const f32x4*>(sTr + bb * BS + l16 * SD + 4 * g4);
+        }
+        // Off the diagonal, T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj), level by
+        // level on the fp32 MFMA; blocks used again later are kept in layout C,
+        // every block is produced in layout R for the output.
+        const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 S;
+        S = mm16(ra[0], tc[0], z);                                    // A10 T00
+        const f32x4 t10c = -mm16(trf[1], S, z), t10r = -mm16(S, trf[1], z);
+        S = mm16(ra[2], tc[1], z);                                    // A21 T11
+        const f32x4 t21c = -mm16(trf[2], S, z), t21r = -mm16(S, trf[2], z);
+        S = mm16(ra[5], tc[2], z);                                    // A32 T22
+        const f32x4 t32r = -mm16(S, trf[3], z);
+        S = mm16(ra[2], t10c, mm16(ra[1], tc[0], z));                 // A20 T00 + A21 T10
+        const f32x4 t20c = -mm16(trf[2], S, z), t20r = -mm16(S, trf[2], z);
+        S = mm16(ra[5], t21c, mm16(ra[4], tc[1], z));                 // A31 T11 + A32 T21
+        const f32x4 t31r = -mm16(S, trf[3], z);
+        S = mm16(ra[5], t20c, mm16(ra[4], t10c, mm16(ra[3], tc[0], z)));   // A30 T00 + A31 T10 + A32 T20
+        const f32x4 t30r = -mm16(S, trf[3], z);
+
+        // T to the workspace as row-operand fragments (tau, ks) = rows 16 tau ..,
+        // k block 32 ks: blocks (tau, 2 ks) and (tau, 2 ks + 1); the two all-zero
+        // fragments (0, 1) and (1, 1) are not written
+        u32x4* Tf = reinterpret_cast<u32x4*>(p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC));
+        auto put = [&](int tau, int ks, f32x4 lo, f32x4 hi) {
+            Tf[(tau * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(lo, hi));
+        };
+        put(0, 0, trf[0], z);
+        put(1, 0, t10r, trf[1]);
+        put(2, 0, t20r, t21r);
+        put(2, 1, trf[2], z);
+        put(3, 0, t30r, t31r);
+        put(3, 1, t32r, trf[3]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -655,10 +727,11 @@ struct Segment {
 
 __device__ __forceinline__ Segment locate_segment(const PrefillParams& p, int g) {
     Segment sg;
-    sg.n = find_seq(p.seg_off, p.n_seqs, g);
-    const int k = g - p.seg_off[sg.n];
-    const int nseg = p.seg_off[sg.n + 1] - p.seg_off[sg.n];
-    const int cs = p.chunk_off[sg.n], ce = p.chunk_off[sg.n + 1];
+    const SeqSpan sp = find_span<true>(p, g);
+    sg.n = sp.n;
+    const int k = g - sp.s0;
+    const int nseg = sp.s1 - sp.s0;
+    const int cs = sp.c0, ce = sp.c1;
     sg.first = k == 0;
     sg.last = k == nseg - 1;
     sg.split = nseg > 1;
@@ -1135,7 +1208,8 @@ __global__ void __launch_bounds__(256) segment_chain_kernel(PrefillParams p) {
     const int h = blockIdx.x / groups;
     const int col = (blockIdx.x - h * groups) * 64 + wave * 16 + l16;
     const int n = blockIdx.y;
-    const int g0 = p.seg_off[n], g1 = p.seg_off[n + 1];
+    const SeqSpan sp = span_of(p, n);
+    const int g0 = sp.s0, g1 = sp.s1;
     if (g1 - g0 < 2) return;                    // not split
     const int dsl = p.dst[n], ssl = p.src[n];
     if (dsl < 0 || dsl >= p.num_slots || ssl >= p.num_slots) return;   // skipped or flagged by pass 3
@@ -1241,7 +1315,7 @@ void launch_recurrence(const PrefillParams& p, int nw, int groups, hipStream_t s
 template <int DK>
 int launch_dk(const PrefillParams& p, int nw, hipStream_t s) {
     if (p.num_chunks > 0) {
-        hipLaunchKernelGGL((prefill_intra_kernel<DK>), dim3(p.num_chunks, p.hv), dim3(64), 0, s, p);
+        hipLaunchKernelGGL((prefill_intra_kernel<DK>), dim3(p.num_chunks, p.hk), dim3(64), 0, s, p);
         const int st = check_launch("intra-chunk");
         if (st != GDN_OK) return st;
     }
@@ -1304,9 +1378,27 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
     p.scale = a->scale;
     p.eps = a->l2_eps;
 
-    hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(kOffThreads), 0, s, p);
-    int st = check_launch("chunk-offset");
-    if (st != GDN_OK) return st;
+    p.inl_n = 0;
+    if (a->num_seqs <= kInlineSeqs) {
+        // first chunk and first segment of every sequence from the host
+        // mirror of cu_seqlens, as the planner counted them
+        int32_t cc = 0, ss = 0;
+        for (int32_t i = 0; i < a->num_seqs; ++i) {
+            p.inl_chunk[i] = cc;
+            p.inl_seg[i] = ss;
+            const int32_t len = a->cu_seqlens_host[i + 1] - a->cu_seqlens_host[i];
+            const int32_t nc = len > 0 ? (len + kC - 1) / kC : 0;
+            cc += nc;
+            ss += (plan.seg_len == 0 || nc <= plan.seg_len) ? 1 : (nc + plan.seg_len - 1) / plan.seg_len;
+        }
+        p.inl_chunk[a->num_seqs] = cc;
+        p.inl_seg[a->num_seqs] = ss;
+        p.inl_n = a->num_seqs;
+    } else {
+        hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(kOffThreads), 0, s, p);
+        const int st = check_launch("chunk-offset");
+        if (st != GDN_OK) return st;
+    }
     const int nw = a->dv >= 64 ? 4 : a->dv / 16;
     switch (a->dk) {
         case 32: return launch_dk<32>(p, nw, s);

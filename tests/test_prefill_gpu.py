@@ -388,3 +388,43 @@ def test_prefill_checkpoint_out_of_range_is_flagged():
     o, st = _gpu_prefill_ckpt(pw, [0], [1], [2, 99, -1], err=err)
     assert int(err.item()) == gdn.GDN_ERRFLAG_SLOT_RANGE
     _check_ckpt(pw, o, st, [0], [1], [2, -1, -1])
+
+
+@pytest.mark.parametrize("n_seqs", [32, 33])
+def test_offset_tables_both_sources(n_seqs):
+    """Calls of at most 32 sequences take the first chunk and segment of every
+    sequence from tables the host puts in the kernel arguments; larger calls
+    have them computed on the GPU. Both sources on the same mix: a split
+    2600-token sequence resuming from a slot, short and empty sequences and a
+    skipped one, with weak decay so every chained state reaches the outputs.
+    One workload of 33 sequences, the last one empty, serves both: the
+    32-sequence call leaves that one out, so the two calls must agree bit for
+    bit on everything else."""
+    import dataclasses
+    rng = np.random.default_rng(83)
+    lengths = [2600] + [int(x) for x in rng.integers(1, 150, size=31)] + [0]
+    lengths[5] = 0
+    lengths[9] = 64
+    src = [0] + [-1 if i % 3 else 0 for i in range(1, 33)]
+    dst = list(range(1, 34))
+    dst[7] = -1
+    pw = prefill_workload("offset_tables", seed=83, lengths=lengths, HK=1, HV=2, dk=128, dv=128, dtype=BF16,
+                          num_slots=34, pool_sigma=0.05, src=src, g_range=(1e-4, 1e-2))
+    if n_seqs == 32:
+        pw = dataclasses.replace(pw, cu_seqlens=pw.cu_seqlens[:33].copy(), src=pw.src[:32].copy())
+        src, dst = src[:32], dst[:32]
+    o, st, _ = _gpu_prefill(pw, src, dst)
+    _check(pw, o, st, src, dst)
+    np.testing.assert_array_equal(st.cpu().numpy()[0], pw.pool[0])
+    if n_seqs == 32:
+        _OFFSET_TABLE_RUN["32"] = (o.cpu(), st.cpu())
+    elif "32" in _OFFSET_TABLE_RUN:
+        torch = _torch()
+        o32, st32 = _OFFSET_TABLE_RUN.pop("32")
+        assert torch.equal(o.cpu().view(torch.int16), o32.view(torch.int16)), \
+            "outputs differ between the two offset-table sources"
+        # (slot 33 receives the empty last sequence's zero state only in the 33-sequence call)
+        assert torch.equal(st.cpu()[:33], st32[:33]), "states differ between the two offset-table sources"
+
+
+_OFFSET_TABLE_RUN = {}
