@@ -865,13 +865,12 @@ prefill_recurrent_kernel(PrefillParams p) {
         }
 #pragma unroll
         for (int m = 0; m < TP; ++m) *reinterpret_cast<u32x4*>(sT + 8 * (htid + S::NB * m)) = rT[m];
-        if (!m_cols) {
+        // (transition columns stage the zeros their empty buffer range loads)
 #pragma unroll
-            for (int m = 0; m < VV; ++m) {
-                const int idx = htid + S::NB * m;
-                const int r = idx / (NV / 8), c8 = idx % (NV / 8);
-                if (idx < S::VP) *reinterpret_cast<u32x4*>(sV + r * SV + c8 * 8) = rV[m];
-            }
+        for (int m = 0; m < VV; ++m) {
+            const int idx = htid + S::NB * m;
+            const int r = idx / (NV / 8), c8 = idx % (NV / 8);
+            if (idx < S::VP) *reinterpret_cast<u32x4*>(sV + r * SV + c8 * 8) = rV[m];
         }
 #pragma unroll
         for (int m = 0; m < SCN; ++m) {
@@ -1035,7 +1034,7 @@ prefill_recurrent_kernel(PrefillParams p) {
             const int r0 = 16 * tau + 4 * g4;
             const f32x4 sx = *reinterpret_cast<const f32x4*>(sSc + kScX * kC + r0);
             const f32x4 sb = *reinterpret_cast<const f32x4*>(sSc + kScBeta * kC + r0);
-            const f32x4 vv = m_cols ? f32x4{0.f, 0.f, 0.f, 0.f} : lds_tr4_f32(sV, SV, 16 * tau, wave * 16, g4, l16);
+            const f32x4 vv = lds_tr4_f32(sV, SV, 16 * tau, wave * 16, g4, l16);
             Y[tau] = sb * (vv - sx * X[tau]);
         }
         const bf16x8 yb0 = pack8(Y[0], Y[1]), yb1 = pack8(Y[2], Y[3]);
