@@ -568,7 +568,8 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
                 else ra[tr * (tr - 1) / 2 + ts] = a;
             }
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) Pf[(tr * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(pt[2 * ks], pt[2 * ks + 1]));
+            for (int ks = 0; ks < 2; ++ks)   // (rows below 32 have an all-zero second k-step: not written)
+                if (ks == 0 || tr >= 2) Pf[(tr * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(pt[2 * ks], pt[2 * ks + 1]));
         }
         lds_barrier();
         {
@@ -834,9 +835,14 @@ prefill_recurrent_kernel(PrefillParams p) {
             const int r = idx / (DK / 8), c8 = idx % (DK / 8);
             rK[m] = buf_load16(kr, 2u * (r * kq_row + c8 * 8));
         }
-        const uint16_t* TPg = p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC);
+        // T fragments; the two all-zero ones, (0, 1) and (1, 1), are never
+        // written by the intra-chunk kernel nor read here (they load as zero)
+        const rsrc_t tr_ = make_rsrc(p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC), 2u * (kC * kC));
 #pragma unroll
-        for (int m = 0; m < TP; ++m) rT[m] = *at_bytes<u32x4>(TPg, 16u * (htid + S::NB * m));
+        for (int m = 0; m < TP; ++m) {
+            const int idx = htid + S::NB * m, frag = idx >> 6;
+            rT[m] = buf_load16(tr_, (frag == 1 || frag == 3) ? kOff : 16u * idx);
+        }
         const rsrc_t vr = make_rsrc(p.v + (static_cast<size_t>(t0) * p.hv + h) * p.dv + vcol0,
                                     m_cols ? 0u : rows_bytes(len, v_row, NV));
 #pragma unroll
@@ -892,9 +898,10 @@ prefill_recurrent_kernel(PrefillParams p) {
         for (int ks = 0; ks < KS; ++ks)
             hr.q[ks] = __builtin_bit_cast(bf16x8, buf_load16(qr, 2u * ((16 * wave + l16) * kq_row + 32 * ks + 8 * g4)));
         // (the second k-step of P is all zero for rows below 32 and is then not used)
-        const uint16_t* Pf = p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC) + kC * kC;
+        const rsrc_t pr_ = make_rsrc(p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC) + kC * kC, 2u * (kC * kC));
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) hr.pr[ks] = *at_bytes<bf16x8>(Pf, 16u * ((wave * 2 + ks) * 64 + lane));
+        for (int ks = 0; ks < 2; ++ks)
+            hr.pr[ks] = __builtin_bit_cast(bf16x8, buf_load16(pr_, (ks == 1 && wave < 2) ? kOff : 16u * ((wave * 2 + ks) * 64 + lane)));
         const float* SCg = p.sc + (static_cast<size_t>(c) * p.hv + h) * (kScRows * kC);
         hr.sz = *at_bytes<f32x4>(SCg, 4u * (kScZ * kC + 16 * wave + 4 * g4));
     };
