@@ -1127,6 +1127,20 @@ prefill_recurrent_kernel(PrefillParams p) {
         }
         return;
     }
+    // store this lane's state entries to a [DK][dv] fp32 tile through a
+    // buffer resource: one lane offset and scalar row offsets (64-bit
+    // per-element addresses would be hoisted out of the chunk loop and held in
+    // registers for the whole pass)
+    auto store_tile = [&](float* tile) {
+        const rsrc_t cr = make_rsrc(tile, 4u * DK * p.dv);
+        const unsigned lo = 4u * (4 * g4 * p.dv + col);
+#pragma unroll
+        for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(H[mu][i]), cr, lo,
+                                                      4u * (16 * mu + i) * p.dv, 0);
+    };
     // periodic checkpoint: the state after chunk c0 + s, when one is requested
     auto checkpoint = [&](int s) {
         if (!OUT || p.ckpt == nullptr) return;
@@ -1136,11 +1150,7 @@ prefill_recurrent_kernel(PrefillParams p) {
             if (tid == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
             return;
         }
-        float* out = p.pool + (static_cast<size_t>(ck) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) out[(16 * mu + 4 * g4 + i) * p.dv + col] = H[mu][i];
+        store_tile(p.pool + (static_cast<size_t>(ck) * p.hv + h) * (static_cast<size_t>(DK) * p.dv));
     };
     if (steps > 0) lds_barrier();
     for (int s = 0; s < steps; s += 2) {
@@ -1160,17 +1170,9 @@ prefill_recurrent_kernel(PrefillParams p) {
 
     if (OUT) {
         if (!sg.last) return;               // a middle segment's end state is the next one's start (pass 2)
-        float* out = p.pool + (static_cast<size_t>(dsl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) out[(16 * mu + 4 * g4 + i) * p.dv + col] = H[mu][i];
+        store_tile(p.pool + (static_cast<size_t>(dsl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv));
     } else if (!m_cols) {
-        float* out = p.se + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) out[(16 * mu + 4 * g4 + i) * p.dv + col] = H[mu][i];
+        store_tile(p.se + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv));
     } else {
         // transition M[d][m] (m = col), as bf16 high part and the bf16 rounding of the remainder
         uint16_t* out = p.sm + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (2 * DK * DK);
