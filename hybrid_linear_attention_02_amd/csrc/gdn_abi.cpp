@@ -134,12 +134,13 @@ static bool prefill_dims_supported(int32_t dk, int32_t dv) {
 // recurrence passes: a pass takes whole rounds of kNumCUs workgroups (one
 // resident per CU), each round as many steps as its longest chain. Costs per
 // step are measured cycle counts of the MI355X kernels: state pass 2800 (per
-// chunk), output pass 3800 (per chunk, one extra step), chain pass 9700 (per
-// segment hop with a transition product; the first segment runs from the true
-// initial state in the state pass, value columns only, and its hop is a copy
-// costed at a third). Returns 0 (no split) when one pass is estimated fastest.
+// chunk), output pass 3800 (per chunk, one extra step), 6000 per transition
+// the output pass's later segments apply before their first chunk (segment k
+// applies k - 1 of them; the first segment runs from the true initial state
+// in the state pass, value columns only, so the second needs none). Returns 0
+// (no split) when one pass is estimated fastest.
 int32_t choose_seg_len(const int32_t* cu, int32_t n, int32_t hv, int32_t dk, int32_t dv) {
-    constexpr double kState = 2800, kOut = 3800, kHop = 9700;
+    constexpr double kState = 2800, kOut = 3800, kHop = 6000;
     const int64_t w_out = static_cast<int64_t>(hv) * (dv / 64);          // workgroups per segment, output pass
     const int64_t w_state = static_cast<int64_t>(hv) * (dv / 64 + dk / 64);  // state pass
     auto pass = [](int64_t wg_steps, int64_t longest) {
@@ -161,7 +162,7 @@ int32_t choose_seg_len(const int32_t* cu, int32_t n, int32_t hv, int32_t dk, int
         }
         if (longest == 0) return 0.0;
         double t = kOut * pass(out_steps, longest);
-        if (hops > 0) t += kState * pass(state_steps, L) + kHop * (static_cast<double>(hops - 1) + 1.0 / 3.0);
+        if (hops > 0) t += kState * pass(state_steps, L) + kHop * static_cast<double>(hops - 1);
         return t;
     };
     // candidates: the longest sequence cut into k equal segments, k = 2 .. 32
@@ -217,7 +218,7 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     if (chunks * a->num_v_heads > INT32_MAX / 2)
         return fail(GDN_E_INVALID, "gdn_prefill_chunked: too many chunks");
     plan->num_chunks = static_cast<int32_t>(chunks);
-    // (the transition columns and the chain pass work in 64-column groups)
+    // (the transition columns and the transition products work in 64-column groups)
     const bool can_split = !f32 && a->dk >= 64 && a->dv >= 64;
     plan->seg_len = can_split ? choose_seg_len(a->cu_seqlens_host, n, a->num_v_heads, a->dk, a->dv) : 0;
     int64_t segs = 0;

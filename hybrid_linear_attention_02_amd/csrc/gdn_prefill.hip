@@ -90,7 +90,7 @@ struct PrefillParams {
     int32_t* seg_off_w;
     float* se;                  // [segs][HV][DK][DV]   local end state E of each segment (split only)
     uint16_t* sm;               // [segs][HV][2][DK][DK] transition M, bf16 high and low parts (split only)
-    float* sh;                  // [segs][HV][DK][DV]   initial state of each segment (split only)
+    float* sh;                  // [segs][HV][DK][DV]   copy of the initial state at a split sequence's first segment
     int32_t seg_len;            // chunks per segment; 0 = one segment per sequence
     int32_t num_segs;
     int32_t n_seqs;
@@ -724,6 +724,8 @@ struct Segment {
     int tb, te;     // token range [tb, te)
     bool first, last;
     bool split;     // the sequence has more than one segment
+    int k;          // index of the segment in its sequence
+    int g0;         // first segment of the sequence
 };
 
 __device__ __forceinline__ Segment locate_segment(const PrefillParams& p, int g) {
@@ -733,6 +735,8 @@ __device__ __forceinline__ Segment locate_segment(const PrefillParams& p, int g)
     const int k = g - sp.s0;
     const int nseg = sp.s1 - sp.s0;
     const int cs = sp.c0, ce = sp.c1;
+    sg.k = k;
+    sg.g0 = sp.s0;
     sg.first = k == 0;
     sg.last = k == nseg - 1;
     sg.split = nseg > 1;
@@ -749,7 +753,8 @@ enum : int {
     kModeState = 1,    // split pass 1: no outputs; columns [0, dv) carry the state from zero with V,
                        // columns [dv, dv + dk) carry the identity with V = 0 (the transition M);
                        // results to the segment buffers. The first segment instead carries the
-                       // true initial state (no transition), so its result is the next start.
+                       // true initial state (no transition), so its result is the next start; the
+                       // output pass carries later segments' starts through the transitions.
 };
 
 // Registers a helper wave loads one step ahead for its output rows.
@@ -978,12 +983,16 @@ prefill_recurrent_kernel(PrefillParams p) {
     if (!helper) {
         const float* init = nullptr;
         if (OUT) {
-            // A split sequence starts every segment, the first included, from
-            // the chained initial states: the source slot is then read only by
-            // the passes before this one, before the last segment may
-            // overwrite it in place.
-            if (sg.split) init = p.sh + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
-            else if (ssl >= 0) init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+            // A split sequence starts its first segment from the state pass's
+            // copy of the initial state (the source slot is then read only by
+            // that pass, before the last segment may overwrite it in place),
+            // its second from the first segment's end state, and later ones
+            // from that state carried through the transitions below.
+            if (sg.split) {
+                init = (sg.k == 0 ? p.sh : p.se) + (static_cast<size_t>(sg.g0) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+            } else if (ssl >= 0) {
+                init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+            }
         } else if (sg.first && ssl >= 0) {
             init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
         }
@@ -1104,6 +1113,29 @@ prefill_recurrent_kernel(PrefillParams p) {
         // the output pass the emission between the loads and the staging
         // covers their latency.
         fetch(c0);
+        if (OUT && sg.split) {
+            // stage each transition the compute waves apply to reach this
+            // segment's initial state (segments 2 and later), high and low
+            // bf16 parts, swizzled like the k tiles, in LDS the pipeline has
+            // not used yet
+            constexpr int MP = 2 * DK * DK / 8 / S::NB;   // 16-byte pieces per helper thread
+            for (int jh = 1; jh < sg.k; ++jh) {
+                const uint16_t* mg = p.sm + (static_cast<size_t>(sg.g0 + jh) * p.hv + h) * (2 * DK * DK);
+                u32x4 rm[MP];
+#pragma unroll
+                for (int m = 0; m < MP; ++m) rm[m] = *at_bytes<u32x4>(mg, 16u * (htid + S::NB * m));
+                uint16_t* sM = reinterpret_cast<uint16_t*>(lds);
+#pragma unroll
+                for (int m = 0; m < MP; ++m) {
+                    const int e0 = 8 * (htid + S::NB * m);   // element of [2][DK][DK]
+                    const int part = e0 / (DK * DK), rem = e0 - part * DK * DK;
+                    const int r = rem / DK, cc = rem - r * DK;
+                    *reinterpret_cast<u32x4*>(sM + part * DK * DK + kq_off<DK, false>(r, cc)) = rm[m];
+                }
+                lds_barrier();        // transition staged
+                lds_barrier();        // compute waves done with it
+            }
+        }
         stage(0);
         if (!OUT) fetch(min(c0 + 1, c1 - 1));
         lds_barrier();
@@ -1152,6 +1184,53 @@ prefill_recurrent_kernel(PrefillParams p) {
         }
         store_tile(p.pool + (static_cast<size_t>(ck) * p.hv + h) * (static_cast<size_t>(DK) * p.dv));
     };
+    if (OUT && sg.split) {
+        // segments 2 and later: H <- M_j H + E_j for the transitions of the
+        // segments before this one (from the first segment's end state), as
+        // bf16 MFMAs on high/low splits of both factors
+        // (M_hi H_hi + M_hi H_lo + M_lo H_hi, about 16 significant bits)
+        const uint16_t* sMh = reinterpret_cast<const uint16_t*>(lds);
+        const uint16_t* sMl = sMh + DK * DK;
+        for (int jh = 1; jh < sg.k; ++jh) {
+            const float* se = p.se + (static_cast<size_t>(sg.g0 + jh) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+            f32x4 acc[MT];
+#pragma unroll
+            for (int mu = 0; mu < MT; ++mu)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mu][i] = se[(16 * mu + 4 * g4 + i) * p.dv + col];
+            bf16x8 bh[KS], bl[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                f32x4 l0, l1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    l0[i] = H[2 * ks][i] - bf16_to_f32(f32_to_bf16(H[2 * ks][i]));
+                    l1[i] = H[2 * ks + 1][i] - bf16_to_f32(f32_to_bf16(H[2 * ks + 1][i]));
+                }
+                bh[ks] = pack8(H[2 * ks], H[2 * ks + 1]);
+                bl[ks] = pack8(l0, l1);
+            }
+            lds_barrier();            // transition staged
+#pragma unroll
+            for (int mu = 0; mu < MT; ++mu) {
+                const int row = 16 * mu + l16;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 ah = kq_pair<DK, false>(sMh, row, 32 * ks, g4);
+                    const bf16x8 al = kq_pair<DK, false>(sMl, row, 32 * ks, g4);
+                    acc[mu] = mfma16(ah, bh[ks], acc[mu]);
+                    acc[mu] = mfma16(ah, bl[ks], acc[mu]);
+                    acc[mu] = mfma16(al, bh[ks], acc[mu]);
+                }
+            }
+#pragma unroll
+            for (int mu = 0; mu < MT; ++mu) H[mu] = acc[mu];
+            lds_barrier();            // done with the transition
+        }
+    }
+    // the state pass keeps a copy of a split sequence's initial state for the
+    // output pass's first segment
+    if (!OUT && sg.first) store_tile(p.sh + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv));
     if (steps > 0) lds_barrier();
     for (int s = 0; s < steps; s += 2) {
         if (s < nch) {
@@ -1189,120 +1268,6 @@ prefill_recurrent_kernel(PrefillParams p) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// split pass 2: chain the segments of each split sequence,
-// H_{s+1} = M_s H_s + E_s, one workgroup per (sequence, value head, 64 value
-// columns), one wave per 16 columns. Writes every segment's initial state:
-// the first one copied from the source slot or zero, the second one equal to
-// the first segment's end state (that segment ran from the true initial
-// state), the rest by the product. The products are bf16 MFMAs on high/low
-// splits of both factors (M_hi H_hi + M_hi H_lo + M_lo H_hi), which keeps
-// about 16 bits of the fp32 state.
-// ---------------------------------------------------------------------------
-
-template <int DK>
-__global__ void __launch_bounds__(256) segment_chain_kernel(PrefillParams p) {
-    constexpr int MT = DK / 16, KS = DK / 32;
-    constexpr int NT = 256;
-    constexpr int MPT = 2 * DK * DK / 8 / NT;   // 16-byte pieces of M (high and low) per thread
-    // M_s, high and low parts, staged whole in LDS per segment (swizzled like
-    // the k tiles: conflict-free row-operand reads)
-    __shared__ __align__(16) uint16_t sMh[DK * DK];
-    __shared__ __align__(16) uint16_t sMl[DK * DK];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int g4 = lane >> 4, l16 = lane & 15;
-    const int groups = p.dv / 64;
-    const int h = blockIdx.x / groups;
-    const int col = (blockIdx.x - h * groups) * 64 + wave * 16 + l16;
-    const int n = blockIdx.y;
-    const SeqSpan sp = span_of(p, n);
-    const int g0 = sp.s0, g1 = sp.s1;
-    if (g1 - g0 < 2) return;                    // not split
-    const int dsl = p.dst[n], ssl = p.src[n];
-    if (dsl < 0 || dsl >= p.num_slots || ssl >= p.num_slots) return;   // skipped or flagged by pass 3
-
-    const size_t tile = static_cast<size_t>(DK) * p.dv;
-    f32x4 H[MT];
-    if (ssl >= 0) {
-        const float* st = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * tile;
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) H[mu][i] = st[(16 * mu + 4 * g4 + i) * p.dv + col];
-    } else {
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu) H[mu] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    {
-        float* sh = p.sh + (static_cast<size_t>(g0) * p.hv + h) * tile;
-        const float* se = p.se + (static_cast<size_t>(g0) * p.hv + h) * tile;
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const size_t e = static_cast<size_t>(16 * mu + 4 * g4 + i) * p.dv + col;
-                sh[e] = H[mu][i];
-                H[mu][i] = se[e];
-            }
-    }
-    for (int g = g0 + 1;; ++g) {
-        float* sh = p.sh + (static_cast<size_t>(g) * p.hv + h) * tile;
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sh[(16 * mu + 4 * g4 + i) * p.dv + col] = H[mu][i];
-        if (g + 1 == g1) break;
-        // issue every load of this segment first: M (all threads), E (own columns)
-        const uint16_t* mg = p.sm + (static_cast<size_t>(g) * p.hv + h) * (2 * DK * DK);
-        u32x4 rm[MPT];
-#pragma unroll
-        for (int m = 0; m < MPT; ++m) rm[m] = *reinterpret_cast<const u32x4*>(mg + 8 * (tid + NT * m));
-        const float* se = p.se + (static_cast<size_t>(g) * p.hv + h) * tile;
-        f32x4 acc[MT];
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mu][i] = se[(16 * mu + 4 * g4 + i) * p.dv + col];
-        // B operands: high and low bf16 parts of H, k = state row
-        bf16x8 bh[KS], bl[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            f32x4 l0, l1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                l0[i] = H[2 * ks][i] - bf16_to_f32(f32_to_bf16(H[2 * ks][i]));
-                l1[i] = H[2 * ks + 1][i] - bf16_to_f32(f32_to_bf16(H[2 * ks + 1][i]));
-            }
-            bh[ks] = pack8(H[2 * ks], H[2 * ks + 1]);
-            bl[ks] = pack8(l0, l1);
-        }
-        lds_barrier();                          // previous segment's LDS reads are done
-#pragma unroll
-        for (int m = 0; m < MPT; ++m) {
-            const int e0 = 8 * (tid + NT * m);   // element of [2][DK][DK]
-            const int part = e0 / (DK * DK), rem = e0 - part * DK * DK;
-            const int r = rem / DK, c = rem - r * DK;
-            *reinterpret_cast<u32x4*>((part ? sMl : sMh) + kq_off<DK, false>(r, c)) = rm[m];
-        }
-        lds_barrier();
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu) {
-            const int row = 16 * mu + l16;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 ah = kq_pair<DK, false>(sMh, row, 32 * ks, g4);
-                const bf16x8 al = kq_pair<DK, false>(sMl, row, 32 * ks, g4);
-                acc[mu] = mfma16(ah, bh[ks], acc[mu]);
-                acc[mu] = mfma16(ah, bl[ks], acc[mu]);
-                acc[mu] = mfma16(al, bh[ks], acc[mu]);
-            }
-        }
-#pragma unroll
-        for (int mu = 0; mu < MT; ++mu) H[mu] = acc[mu];
-    }
-}
-
 int check_launch(const char* what) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -1333,10 +1298,6 @@ int launch_dk(const PrefillParams& p, int nw, hipStream_t s) {
         // transition (dk identity columns), all segments at once
         launch_recurrence<DK, kModeState>(p, nw, groups + DK / (16 * nw), s);
         int st = check_launch("segment state pass");
-        if (st != GDN_OK) return st;
-        // pass 2: chain the segments
-        hipLaunchKernelGGL((segment_chain_kernel<DK>), dim3(p.hv * (p.dv / 64), p.n_seqs), dim3(256), 0, s, p);
-        st = check_launch("segment chain");
         if (st != GDN_OK) return st;
     }
     launch_recurrence<DK, kModeOutput>(p, nw, groups, s);
