@@ -327,7 +327,9 @@ typedef struct gdn_prefill_args {
     int32_t num_seqs;             /* N >= 0 */
     int32_t total_tokens;         /* T = cu_seqlens[N] */
     const int32_t* cu_seqlens;    /* [N+1] device, 0 = cu[0] <= cu[1] <= ... */
-    const int32_t* cu_seqlens_host; /* [N+1] host mirror (grid sizing, checks) */
+    const int32_t* cu_seqlens_host; /* [N+1] host mirror, equal to cu_seqlens: grid sizing,
+                                     checks, and for N <= 32 the first chunk of every
+                                     sequence, passed to the kernels by value */
     int32_t chunk_size;           /* must be 64 */
     int32_t num_k_heads, num_v_heads, dk, dv;
     int32_t dtype;                /* GDN_DTYPE_BF16: chunked form on bf16 matrix cores, dk in
