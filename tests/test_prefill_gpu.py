@@ -428,3 +428,18 @@ def test_offset_tables_both_sources(n_seqs):
 
 
 _OFFSET_TABLE_RUN = {}
+
+
+def test_split_sequences_after_others_carry_transitions():
+    """Two split sequences that are not the first of the call (their first
+    segment is not segment 0 of the call), one resuming in place, with weak
+    decay: every later segment's start comes from transitions applied before
+    its first chunk, indexed from that sequence's own first segment."""
+    lengths = [100, 70, 2600, 0, 1500]
+    src = [0, -1, 2, 1, -1]
+    dst = [3, 4, 2, 5, 6]
+    pw = prefill_workload("split_after_others", seed=89, lengths=lengths, HK=1, HV=2, dk=128, dv=128,
+                          dtype=BF16, num_slots=7, pool_sigma=0.05, src=src, g_range=(1e-4, 1e-2))
+    o, st, _ = _gpu_prefill(pw, src, dst)
+    _check(pw, o, st, src, dst)
+    np.testing.assert_array_equal(st.cpu().numpy()[[0, 1]], pw.pool[[0, 1]])
