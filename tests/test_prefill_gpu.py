@@ -443,3 +443,18 @@ def test_split_sequences_after_others_carry_transitions():
     o, st, _ = _gpu_prefill(pw, src, dst)
     _check(pw, o, st, src, dst)
     np.testing.assert_array_equal(st.cpu().numpy()[[0, 1]], pw.pool[[0, 1]])
+
+
+def test_split_full_heads_in_place():
+    """One 4096-token sequence at 16/32 heads, 128 x 128, resuming in place
+    from a pool state with weak decay: the planner splits it into three
+    segments of up to 22 chunks at the full head count, so the state pass
+    fills most of the chip and the third segment applies a transition. The
+    oracle follows value heads 0, 1, 30 and 31."""
+    src = [1]
+    dst = [1]
+    pw = prefill_workload("split_full_heads_inplace", seed=97, lengths=[4096], HK=16, HV=32, dk=128, dv=128,
+                          dtype=BF16, num_slots=2, pool_sigma=0.05, src=src, g_range=(1e-4, 1e-2))
+    o, st, _ = _gpu_prefill(pw, src, dst)
+    _check(pw, o, st, src, dst, heads=[0, 1, 30, 31])
+    np.testing.assert_array_equal(st.cpu().numpy()[0], pw.pool[0])
