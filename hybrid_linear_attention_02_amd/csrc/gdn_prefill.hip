@@ -144,19 +144,6 @@ __device__ __forceinline__ SeqSpan find_span(const PrefillParams& p, int key) {
     return SeqSpan{lo, p.chunk_off[lo], p.chunk_off[lo + 1], p.seg_off[lo], p.seg_off[lo + 1]};
 }
 
-// The span of sequence n (wave-uniform).
-__device__ __forceinline__ SeqSpan span_of(const PrefillParams& p, int n) {
-    if (p.inl_n > 0) {
-        SeqSpan r{0, p.inl_chunk[0], p.inl_chunk[1], p.inl_seg[0], p.inl_seg[1]};
-        if (p.inl_n == 1) return r;
-#pragma unroll
-        for (int i = 1; i < kInlineSeqs; ++i)
-            if (i == n) r = SeqSpan{i, p.inl_chunk[i], p.inl_chunk[i + 1], p.inl_seg[i], p.inl_seg[i + 1]};
-        return r;
-    }
-    return SeqSpan{n, p.chunk_off[n], p.chunk_off[n + 1], p.seg_off[n], p.seg_off[n + 1]};
-}
-
 // Uniform base pointer plus a 32-bit per-lane byte offset: lets the compiler
 // use the scalar-base global access form (no 64-bit address per lane).
 template <typename T, typename B>
