@@ -278,11 +278,12 @@ def bench_prefill(reps=20, warmup=3):
     }
 
 
-def bench_prefill_packed(reps=5):
+def bench_prefill_packed(reps=10, warmup=3):
     """Chunked prefill of the long/packed workload: one 50,000-token sequence
     plus 16 sequences of U[1K, 16K] tokens in one call, zero initial states,
     16/32 heads, 128 x 128 bf16. Many independent (sequence, head) chains fill
-    more of the chip than the single 8192-token sequence."""
+    more of the chip than the single 8192-token sequence. `warmup` untimed
+    calls, then `reps` calls back to back between two events."""
     import torch
     from hybrid_linear_attention_02_amd import gdn
     from hybrid_linear_attention_02_amd.workloads import long_packed_prefill
@@ -301,6 +302,8 @@ def bench_prefill_packed(reps=5):
     src = torch.full((N,), -1, dtype=torch.int32, device="cuda")
     dst = torch.arange(1, N + 1, dtype=torch.int32, device="cuda")
     ws = gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src, dst)
+    for _ in range(warmup - 1):
+        gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src, dst, workspace=ws)
     torch.cuda.synchronize()
     a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
