@@ -1000,6 +1000,20 @@ prefill_recurrent_kernel(PrefillParams p) {
         const uint16_t* sT = tile16(S::L_T, b, S::SZ_T);
         const uint16_t* sV = tile16(S::L_V, b, S::SZ_V);
         const float* sSc = reinterpret_cast<const float*>(lds + S::L_SC + b * S::SZ_SC);
+        // state pass: the Y operands do not depend on the state, so they are
+        // requested before the X products (the output pass has no registers
+        // to spare for them)
+        f32x4 ysx[4], ysb[4], yv[4];
+        if (!OUT) {
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+                const int r0 = 16 * tau + 4 * g4;
+                ysx[tau] = *reinterpret_cast<const f32x4*>(sSc + kScX * kC + r0);
+                ysb[tau] = *reinterpret_cast<const f32x4*>(sSc + kScBeta * kC + r0);
+                yv[tau] = lds_tr4_f32(sV, SV, 16 * tau, wave * 16, g4, l16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         bf16x8 hb[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) hb[ks] = pack8(H[2 * ks], H[2 * ks + 1]);
@@ -1034,11 +1048,15 @@ prefill_recurrent_kernel(PrefillParams p) {
         f32x4 Y[4];
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
-            const int r0 = 16 * tau + 4 * g4;
-            const f32x4 sx = *reinterpret_cast<const f32x4*>(sSc + kScX * kC + r0);
-            const f32x4 sb = *reinterpret_cast<const f32x4*>(sSc + kScBeta * kC + r0);
-            const f32x4 vv = lds_tr4_f32(sV, SV, 16 * tau, wave * 16, g4, l16);
-            Y[tau] = sb * (vv - sx * X[tau]);
+            if (!OUT) {
+                Y[tau] = ysb[tau] * (yv[tau] - ysx[tau] * X[tau]);
+            } else {
+                const int r0 = 16 * tau + 4 * g4;
+                const f32x4 sx = *reinterpret_cast<const f32x4*>(sSc + kScX * kC + r0);
+                const f32x4 sb = *reinterpret_cast<const f32x4*>(sSc + kScBeta * kC + r0);
+                const f32x4 vv = lds_tr4_f32(sV, SV, 16 * tau, wave * 16, g4, l16);
+                Y[tau] = sb * (vv - sx * X[tau]);
+            }
         }
         const bf16x8 yb0 = pack8(Y[0], Y[1]), yb1 = pack8(Y[2], Y[3]);
         // U = T Y   (T lower triangular: skip the all-zero upper k-step); T
