@@ -1000,10 +1000,11 @@ prefill_recurrent_kernel(PrefillParams p) {
         const uint16_t* sT = tile16(S::L_T, b, S::SZ_T);
         const uint16_t* sV = tile16(S::L_V, b, S::SZ_V);
         const float* sSc = reinterpret_cast<const float*>(lds + S::L_SC + b * S::SZ_SC);
-        // state pass: the Y operands do not depend on the state, so they are
-        // requested before the X products (the output pass has no registers
-        // to spare for them)
-        f32x4 ysx[4], ysb[4], yv[4];
+        // state pass: the operands of Y, U and DU (scale rows, V, the T
+        // fragments) do not depend on the state, so they are requested before
+        // the X products (the output pass has no registers to spare for them)
+        f32x4 ysx[4], ysb[4], yv[4], ysd[4];
+        bf16x8 ytf[6];
         if (!OUT) {
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
@@ -1012,6 +1013,13 @@ prefill_recurrent_kernel(PrefillParams p) {
                 ysb[tau] = *reinterpret_cast<const f32x4*>(sSc + kScBeta * kC + r0);
                 yv[tau] = lds_tr4_f32(sV, SV, 16 * tau, wave * 16, g4, l16);
             }
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                const int tau = i < 4 ? i : i - 2, ks = i < 4 ? 0 : 1;
+                ytf[i] = *reinterpret_cast<const bf16x8*>(sT + 8 * ((tau * 2 + ks) * 64 + lane));
+            }
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) ysd[tau] = *reinterpret_cast<const f32x4*>(sSc + kScD * kC + 16 * tau + 4 * g4);
             __builtin_amdgcn_sched_barrier(0);
         }
         bf16x8 hb[KS];
@@ -1062,6 +1070,7 @@ prefill_recurrent_kernel(PrefillParams p) {
         // U = T Y   (T lower triangular: skip the all-zero upper k-step); T
         // is staged as row-operand fragments, one kilobyte each
         auto tfrag = [&](int tau, int ks) {
+            if (!OUT) return ytf[ks == 0 ? tau : tau + 2];
             return *reinterpret_cast<const bf16x8*>(sT + 8 * ((tau * 2 + ks) * 64 + lane));
         };
         f32x4 U[4];
@@ -1079,7 +1088,7 @@ prefill_recurrent_kernel(PrefillParams p) {
         f32x4 DU[4];
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
-            const f32x4 sd = *reinterpret_cast<const f32x4*>(sSc + kScD * kC + 16 * tau + 4 * g4);
+            const f32x4 sd = OUT ? *reinterpret_cast<const f32x4*>(sSc + kScD * kC + 16 * tau + 4 * g4) : ysd[tau];
             DU[tau] = sd * U[tau];
         }
         const bf16x8 db0 = pack8(DU[0], DU[1]), db1 = pack8(DU[2], DU[3]);
