@@ -13,6 +13,10 @@ Also measured in the same run (the metric has two halves):
   * chunked prefill of one 8192-token bf16 sequence (same head shape), reported
     under "prefill" as tokens/s and algorithmic MFMA flops against the bf16
     dense peak;
+  * the long/packed prefill (219K tokens in 17 sequences), the multi-turn
+    resume (16 x 800 tokens from 4 shared checkpoints, then 32 decode steps at
+    B = 16), fp32-input prefill, speculative verify, state pack/unpack and
+    recorded decode layer stacks, each under its own key;
   * the fp64 CPU oracle on a bounded sample of the decode workload
     ("cpu_baseline", rank 0, one GPU only).
 
@@ -318,6 +322,87 @@ def bench_prefill_packed(reps=10, warmup=3):
     return {"workload": f"long_packed_prefill_bf16_{N}seqs_t{T}_hk16_hv32_128x128", "tokens": T, "ms": round(t * 1e3, 3),
             "tok_per_s": round(T / t, 1), "tflops_algorithmic": round(tflops, 1),
             "frac_bf16_mfma": round(tflops / BF16_PEAK_TFLOPS, 4)}
+
+
+def bench_resume(reps=20, warmup=3):
+    """Multi-turn resume: 16 sequences of 800 bf16 tokens resume from 4 shared
+    checkpoint slots into fresh slots (the checkpoints are only read), then
+    32 decode steps at B = 16 in place on the fresh slots, 16/32 heads,
+    128 x 128. The prefill is timed as `reps` calls back to back (each call
+    reads the same checkpoints and rewrites the same fresh slots); the 32
+    decode steps are recorded once as a HIP graph and replayed."""
+    import torch
+    from hybrid_linear_attention_02_amd import gdn
+    from hybrid_linear_attention_02_amd.workloads import multiturn_resume
+
+    pw, dec = multiturn_resume()
+    tk = pw.tokens
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, g, b = bf(tk.q), bf(tk.k), bf(tk.v), dev(tk.g), dev(tk.beta)
+    T = int(pw.cu_seqlens[-1])
+    N = len(pw.cu_seqlens) - 1
+    storage = dev(pw.pool)
+    pool = gdn.gdn_state_pool_create(pw.num_slots, pw.HV, pw.dk, pw.dv, storage=storage)
+    ck = pool.alloc(4)
+    for c in ck:
+        for _ in range(4):
+            pool.retain(c)
+    src = [int(s) for s in pw.src]
+    dst = [pool.cow(s) for s in src]
+    pool.validate(src, dst)
+    src_t = torch.tensor(src, dtype=torch.int32, device="cuda")
+    dst_t = torch.tensor(dst, dtype=torch.int32, device="cuda")
+    cu = dev(pw.cu_seqlens)
+    o = torch.empty((T, pw.HV, pw.dv), dtype=torch.bfloat16, device="cuda")
+    ws = gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src_t, dst_t)
+    for _ in range(warmup - 1):
+        gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src_t, dst_t, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, pw.cu_seqlens, src_t, dst_t, workspace=ws)
+    e.record(stream)
+    torch.cuda.synchronize()
+    t_pre = a.elapsed_time(e) / reps * 1e-3
+    flops = T * prefill_flops_per_token(pw.HV, pw.dk, pw.dv)
+    state_bytes = pw.HV * pw.dk * pw.dv * 4
+    pre_bytes = T * prefill_bytes_per_token(pw.HK, pw.HV, pw.dk, pw.dv) + 2 * N * state_bytes
+
+    # decode: 32 steps in place on the fresh slots, recorded once
+    inputs = [(bf(t.q), bf(t.k), bf(t.v), dev(t.g), dev(t.beta)) for t in dec]
+    od = torch.empty((N, pw.HV, pw.dv), dtype=torch.bfloat16, device="cuda")
+    for i in range(min(warmup, len(inputs))):
+        gdn.gdn_decode_step(pool, *inputs[i], od, dst_t, dst_t)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for inp in inputs:
+            gdn.gdn_decode_step(pool, *inp, od, dst_t, dst_t)
+    torch.cuda.synchronize()
+    a.record(stream)
+    graph.replay()
+    e.record(stream)
+    torch.cuda.synchronize()
+    t_dec = a.elapsed_time(e) / len(inputs) * 1e-3
+    dec_bytes = N * decode_bytes_per_request(pw.HK, pw.HV, pw.dk, pw.dv, 2)
+    del graph
+    pool.close()
+    del ws, o, q, k, v, storage
+    return {"workload": f"multiturn_resume_bf16_{N}x{T // N}_from_4_checkpoints_then_{len(inputs)}_decode_steps_b{N}",
+            "prefill_ms": round(t_pre * 1e3, 4), "prefill_tok_per_s": round(T / t_pre, 1),
+            "prefill_tflops_algorithmic": round(flops / t_pre / 1e12, 1),
+            "prefill_frac_bf16_mfma": round(flops / t_pre / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "prefill_gbs_algorithmic": round(pre_bytes / t_pre / 1e9, 1),
+            "decode_us_per_step": round(t_dec * 1e6, 2), "decode_bytes_per_step": dec_bytes,
+            "decode_gbs": round(dec_bytes / t_dec / 1e9, 1),
+            "decode_frac_hbm": round(dec_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4),
+            "timing": "prefill: back-to-back calls between two events; decode: HIP-graph replay of the 32 steps",
+            "note": "the 16 fresh slots (32 MiB of state) stay in the 256 MB MALL between decode steps"}
 
 
 def bench_prefill_f32(reps=5):
@@ -806,6 +891,7 @@ def main():
         pre["cpu_baseline"] = cpu_pre
     pre32 = None if args.no_prefill else bench_prefill_f32()
     packed = None if args.no_prefill else bench_prefill_packed()
+    resume = None if args.no_prefill else bench_resume()
     ver = bench_verify()
     xfer = bench_transfer()
     grf = bench_graph()
@@ -848,6 +934,7 @@ def main():
         "decode_graph": grf,
         "prefill": pre,
         "prefill_packed": packed,
+        "resume": resume,
         "prefill_f32": pre32,
     }
     print(json.dumps(line))
