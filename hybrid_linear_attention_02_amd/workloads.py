@@ -209,11 +209,17 @@ def multiturn_resume(tokens_per_seq=800, decode_steps=32):
     return pw, dec
 
 
+def long_packed_lengths(first=50_000, n_short=16, lo=1024, hi=16384, seed=4) -> list:
+    """Sequence lengths of the long/packed workload: the first sequence, then
+    n_short lengths uniform in [lo, hi] (inclusive)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [first] + [int(x) for x in rng.integers(lo, hi, size=n_short, endpoint=True)]
+
+
 def long_packed_prefill(first=50_000, n_short=16, lo=1024, hi=16384, seed=4) -> PrefillWorkload:
     """One 50,000-token sequence plus 16 sequences with lengths uniform in
     [1024, 16384] (inclusive), packed via cu_seqlens, zero initial states."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    lengths = [first] + [int(x) for x in rng.integers(lo, hi, size=n_short, endpoint=True)]
+    lengths = long_packed_lengths(first, n_short, lo, hi, seed)
     return prefill_workload("long_packed_prefill_bf16_h32_128x128", seed=seed + 100, lengths=lengths,
                             HK=16, HV=32, dk=128, dv=128, dtype=BF16, num_slots=len(lengths) + 1)
 

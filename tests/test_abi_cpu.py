@@ -391,3 +391,44 @@ def test_prefill_unsupported_head_dim(lib):
     n = c_size_t()
     assert lib.gdn_prefill_workspace_bytes(h, byref(a), byref(n)) == gdn.GDN_E_UNSUPPORTED
     lib.gdn_state_pool_destroy(h)
+
+
+def _planned_segments(lib, cu, hv, dk, dv):
+    """Segments the planner gives a call, read from the workspace size: the
+    split sections (end state E and initial state fp32 dk x dv, transition M
+    as bf16 high and low dk x dk, per segment and value head) come after the
+    offset tables, the T/P fragments and the scale rows; with no split they
+    are empty (0 is returned)."""
+    buf, h = _make_pool(lib, hv=hv, dk=dk, dv=dv)
+    _, addr = _fake_storage()
+    cuh = np.asarray(cu, np.int32)
+    a = _prefill_args(addr, cuh, num_k_heads=hv // 2, num_v_heads=hv, dk=dk, dv=dv)
+    n = c_size_t()
+    assert lib.gdn_prefill_workspace_bytes(h, byref(a), byref(n)) == gdn.GDN_OK
+    lib.gdn_state_pool_destroy(h)
+    up = lambda x: (x + 255) // 256 * 256
+    N = len(cu) - 1
+    chunks = int(np.sum((np.diff(np.asarray(cu, np.int64)) + 63) // 64))
+    base = 2 * up(4 * (N + 1)) + up(2 * chunks * hv * 2 * 64 * 64) + up(4 * chunks * hv * 5 * 64)
+    per_seg = hv * (8 * dk * dv + 4 * dk * dk)
+    extra = n.value - base
+    assert extra >= 0 and extra % per_seg == 0
+    return extra // per_seg
+
+
+def test_planner_split_decisions(lib):
+    # one 8192-token sequence at 32 value heads: three segments of 43 chunks
+    assert _planned_segments(lib, [0, 8192], 32, 128, 128) == 3
+    # 16 sequences of 800 tokens fill the chip without a split
+    assert _planned_segments(lib, list(range(0, 16 * 800 + 1, 800)), 32, 128, 128) == 0
+    # the long/packed workload: the 50,000-token sequence in three segments, the
+    # 16 others (at most 256 chunks) whole: 19 segments
+    from hybrid_linear_attention_02_amd.workloads import long_packed_lengths
+    cu = [0] + [int(x) for x in np.cumsum(long_packed_lengths())]
+    assert _planned_segments(lib, cu, 32, 128, 128) == 19
+    # few heads leave the chip idle: a 3,000-token sequence is split, also at 64 value columns
+    for dk, dv in ((128, 128), (64, 64), (128, 64)):
+        assert _planned_segments(lib, [0, 3000, 3090], 4, dk, dv) > 2
+    # transitions work in 64-column groups: no split below 64
+    assert _planned_segments(lib, [0, 3000, 3090], 4, 32, 128) == 0
+    assert _planned_segments(lib, [0, 3000, 3090], 4, 128, 32) == 0

@@ -92,7 +92,7 @@ def test_prefill_varlen_ragged_and_empty():
     np.testing.assert_array_equal(st.cpu().numpy()[:6], before[:6])
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128), (32, 16), (128, 32), (64, 64), (32, 128)])
+@pytest.mark.parametrize("dk,dv", [(dk, dv) for dk in (32, 64, 128) for dv in (16, 32, 64, 128)])
 def test_prefill_head_shapes(dk, dv):
     lengths = [70, 129]
     src = [0, -1]
@@ -306,6 +306,21 @@ def test_split_dk_ne_dv():
                           num_slots=3, pool_sigma=0.05, src=src, g_range=(1e-3, 5e-2))
     o, st, _ = _gpu_prefill(pw, src, dst)
     _check(pw, o, st, src, dst)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64)])
+def test_split_value_width_64(dk, dv):
+    """Split path with 64 value columns (one value-column workgroup per head;
+    the state pass adds dk / 64 transition workgroups): a 3000-token sequence
+    from a pool state beside a short one from zero, weak decay."""
+    lengths = [3000, 90]
+    src = [0, -1]
+    dst = [1, 2]
+    pw = prefill_workload(f"split_{dk}x{dv}", seed=73 + dk, lengths=lengths, HK=2, HV=4, dk=dk, dv=dv, dtype=BF16,
+                          num_slots=3, pool_sigma=0.05, src=src, g_range=(1e-3, 5e-2))
+    o, st, _ = _gpu_prefill(pw, src, dst)
+    _check(pw, o, st, src, dst)
+    np.testing.assert_array_equal(st.cpu().numpy()[0], pw.pool[0])
 
 
 def _gpu_prefill_ckpt(pw, src, dst, ckpt, err=None):
