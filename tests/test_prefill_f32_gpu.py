@@ -143,3 +143,17 @@ def test_prefill_f32_one_long_sequence_full_heads():
                           num_slots=2, pool_sigma=0.05, src=src)
     og, got = _run(pw, src, dst)
     _check(pw, src, dst, og, got)
+
+
+def test_prefill_f32_only_empty_sequences():
+    """fp32 inputs, every sequence empty: sources copied byte for byte, zero
+    for src < 0, one entry in place."""
+    src = [-1, 0, 1]
+    dst = [2, 3, 1]
+    pw = prefill_workload("f32_all_empty", seed=93, lengths=[0, 0, 0], HK=1, HV=2, dk=64, dv=32, dtype=F32,
+                          num_slots=4, pool_sigma=0.05, src=src)
+    og, got = _run(pw, src, dst)
+    assert og.shape[0] == 0
+    np.testing.assert_array_equal(got[2], np.zeros_like(got[2]))
+    np.testing.assert_array_equal(got[3], pw.pool[0])
+    np.testing.assert_array_equal(got[:2], pw.pool[:2])

@@ -323,6 +323,22 @@ def test_split_value_width_64(dk, dv):
     np.testing.assert_array_equal(st.cpu().numpy()[0], pw.pool[0])
 
 
+def test_prefill_only_empty_sequences():
+    """A call whose sequences are all empty (no token, no chunk): every
+    destination receives its source state byte for byte, zero for src < 0,
+    one entry in place."""
+    src = [-1, 0, 1]
+    dst = [2, 3, 1]
+    pw = prefill_workload("all_empty", seed=91, lengths=[0, 0, 0], HK=1, HV=2, dk=128, dv=128, dtype=BF16,
+                          num_slots=4, pool_sigma=0.05, src=src)
+    o, st, _ = _gpu_prefill(pw, src, dst)
+    got = st.cpu().numpy()
+    assert o.shape[0] == 0
+    np.testing.assert_array_equal(got[2], np.zeros_like(got[2]))
+    np.testing.assert_array_equal(got[3], pw.pool[0])
+    np.testing.assert_array_equal(got[:2], pw.pool[:2])
+
+
 def _gpu_prefill_ckpt(pw, src, dst, ckpt, err=None):
     torch = _torch()
     tk = pw.tokens
