@@ -13,7 +13,8 @@ Also measured in the same run (the metric has two halves):
   * chunked prefill of one 8192-token bf16 sequence (same head shape), reported
     under "prefill" as tokens/s and algorithmic MFMA flops against the bf16
     dense peak;
-  * the long/packed prefill (219K tokens in 17 sequences), the multi-turn
+  * the long/packed prefill (219K tokens in 17 sequences), one 1M-token
+    prefill (the longest context of the pages' table), the multi-turn
     resume (16 x 800 tokens from 4 shared checkpoints, then 32 decode steps at
     B = 16), fp32-input prefill, speculative verify, state pack/unpack and
     recorded decode layer stacks, each under its own key;
@@ -421,6 +422,49 @@ def bench_resume(reps=20, warmup=3):
             "decode_frac_hbm": round(dec_bytes / t_dec / 1e9 / HBM_PEAK_GBS, 4),
             "timing": "prefill: back-to-back calls between two events; decode: HIP-graph replay of the 32 steps",
             "note": "the 16 fresh slots (32 MiB of state) stay in the 256 MB MALL between decode steps"}
+
+
+def bench_prefill_long_context(tokens=1 << 20, reps=3):
+    """Chunked prefill of one 1,048,576-token sequence at the batched head
+    shape (16/32 heads, 128 x 128, bf16), the longest context of the pages'
+    long-context table; inputs drawn on the device from a seeded generator
+    (q, k, v ~ N(0, 1), g = -U(0.01, 0.5), beta = sigmoid(N(0, 1))), zero
+    initial state. One untimed call, then `reps` calls back to back."""
+    import torch
+    from hybrid_linear_attention_02_amd import gdn
+
+    HK, HV, DK, DV = 16, 32, 128, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20)
+    q = torch.randn((tokens, HK, DK), generator=gen, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn((tokens, HK, DK), generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn((tokens, HV, DV), generator=gen, device="cuda", dtype=torch.bfloat16)
+    g = -(0.01 + 0.49 * torch.rand((tokens, HV), generator=gen, device="cuda"))
+    b = torch.sigmoid(torch.randn((tokens, HV), generator=gen, device="cuda"))
+    o = torch.empty((tokens, HV, DV), dtype=torch.bfloat16, device="cuda")
+    pool = gdn.gdn_state_pool_create(2, HV, DK, DV)
+    pool.alloc(2)
+    cu_host = np.asarray([0, tokens], np.int32)
+    cu = torch.from_numpy(cu_host).cuda()
+    src = torch.tensor([-1], dtype=torch.int32, device="cuda")
+    dst = torch.tensor([1], dtype=torch.int32, device="cuda")
+    ws = gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, cu_host, src, dst)
+    torch.cuda.synchronize()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        gdn.gdn_prefill_chunked(pool, q, k, v, g, b, o, cu, cu_host, src, dst, workspace=ws)
+    e.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(e) / reps * 1e-3
+    tflops = tokens * prefill_flops_per_token(HV, DK, DV) / t / 1e12
+    pool.close()
+    del q, k, v, g, b, o, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"long_context_prefill_bf16_t{tokens}_hk16_hv32_128x128", "tokens": tokens,
+            "ms": round(t * 1e3, 3), "tok_per_s": round(tokens / t, 1), "tflops_algorithmic": round(tflops, 1),
+            "frac_bf16_mfma": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "data": "synthetic, drawn on the device from a seeded generator"}
 
 
 def bench_prefill_f32(reps=5):
@@ -910,6 +954,7 @@ def main():
     pre32 = None if args.no_prefill else bench_prefill_f32()
     packed = None if args.no_prefill else bench_prefill_packed()
     resume = None if args.no_prefill else bench_resume()
+    long_ctx = None if args.no_prefill else bench_prefill_long_context()
     ver = bench_verify()
     xfer = bench_transfer()
     grf = bench_graph()
@@ -953,6 +998,7 @@ def main():
         "prefill": pre,
         "prefill_packed": packed,
         "resume": resume,
+        "prefill_long_context": long_ctx,
         "prefill_f32": pre32,
     }
     print(json.dumps(line))
