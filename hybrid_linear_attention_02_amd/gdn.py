@@ -505,19 +505,48 @@ def gdn_decode_verify(pool: StatePool, q, k, v, g, beta, o, src_slots, dst_slots
 
 
 def _prefill_args(pool, q, k, v, g, beta, o, cu_seqlens, cu_seqlens_host, src_slots, dst_slots,
-                  scale, l2_eps, err_flag, ckpt_slots=None):
+                  scale, l2_eps, err_flag, ckpt_slots=None, *, full=True):
+    """The gdn_prefill_args struct. With ``full`` every tensor is checked
+    against the shapes q [T, HK, dk] and v [T, HV, dv] fix (k, o, g, beta, the
+    slot tables, the device cu_seqlens): a wrong size would otherwise reach
+    the kernels as a raw pointer. ``full=False`` (workspace sizing) reads only
+    the shapes of q and v."""
     import torch
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [T, HK, dk] and v [T, HV, dv]")
     T, HK, dk = q.shape
     HV, dv = v.shape[1], v.shape[2]
+    if v.shape[0] != T:
+        raise ValueError("q and v must have the same number of tokens")
     host = np.ascontiguousarray(np.asarray(cu_seqlens_host, np.int32))
+    if host.ndim != 1 or host.size < 1:
+        raise ValueError("cu_seqlens_host must be a 1-D table of N + 1 offsets")
     N = len(host) - 1
+    if full:
+        _dtype_code(q)
+        for t, n in ((k, "k"), (v, "v"), (o, "o")):
+            if t.dtype != q.dtype:
+                raise ValueError(f"{n} must have q's dtype")
+        if tuple(k.shape) != (T, HK, dk):
+            raise ValueError(f"k must be [T, HK, dk] = {(T, HK, dk)}")
+        if tuple(o.shape) != (T, HV, dv):
+            raise ValueError(f"o must be [T, HV, dv] = {(T, HV, dv)}")
+        for t, n in ((g, "g"), (beta, "beta")):
+            if t is None or tuple(t.shape) != (T, HV):
+                raise ValueError(f"{n} must be float32 [T, HV] = {(T, HV)}")
+        if src_slots is None or dst_slots is None or src_slots.numel() != N or dst_slots.numel() != N:
+            raise ValueError(f"src_slots and dst_slots must have N = {N} entries")
+        if cu_seqlens is None or cu_seqlens.numel() != N + 1:
+            raise ValueError(f"cu_seqlens (device) must have N + 1 = {N + 1} entries")
+        if err_flag is not None and err_flag.numel() < 1:
+            raise ValueError("err_flag must hold one int32")
     a = PrefillArgs()
     a.num_seqs, a.total_tokens, a.chunk_size = N, T, 64
     a.num_k_heads, a.num_v_heads, a.dk, a.dv = HK, HV, dk, dv
     a.dtype = _dtype_code(q)
     a.cu_seqlens = _dev(cu_seqlens, "cu_seqlens", torch.int32) if cu_seqlens is not None else None
     a.cu_seqlens_host = host.ctypes.data
-    if T > 0:
+    if T > 0 and full:
         a.q, a.k, a.v, a.o = _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o")
         a.g, a.beta = _dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32)
     if src_slots is not None:
@@ -536,7 +565,8 @@ def _prefill_args(pool, q, k, v, g, beta, o, cu_seqlens, cu_seqlens_host, src_sl
 
 def gdn_prefill_workspace_bytes(pool: StatePool, q, v, cu_seqlens_host) -> int:
     """Workspace bytes for a prefill of these shapes (q: [T, HK, dk], v: [T, HV, dv])."""
-    a, host = _prefill_args(pool, q, q, v, None, None, v, None, cu_seqlens_host, None, None, None, 1e-6, None)
+    a, host = _prefill_args(pool, q, q, v, None, None, v, None, cu_seqlens_host, None, None, None, 1e-6, None,
+                            full=False)
     n = c_size_t()
     _check(load_library().gdn_prefill_workspace_bytes(c_void_p(pool.handle), byref(a), byref(n)))
     return int(n.value)
@@ -560,6 +590,14 @@ def gdn_prefill_chunked(pool: StatePool, q, k, v, g, beta, o, cu_seqlens, cu_seq
     _check(load_library().gdn_prefill_workspace_bytes(c_void_p(pool.handle), byref(a), byref(n)))
     if workspace is None:
         workspace = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=q.device)
+    elif not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
     _check(load_library().gdn_prefill_chunked(c_void_p(pool.handle), byref(a), c_void_p(workspace.data_ptr()),
-                                              workspace.numel(), _stream(stream)))
+                                              nbytes, _stream(stream)))
+    if stream is not None and stream != torch.cuda.current_stream():
+        # the caching allocator ties a block to the stream it was made on;
+        # the kernels use it on `stream`, so it must not be reused before
+        # that stream's work ends
+        workspace.record_stream(stream)
     return workspace

@@ -18,6 +18,12 @@ a 50K-token first turn, then 800-token turns -- and the head shape of a
 * Pool tiles ~ N(0, sigma) float32.
 * Generator: numpy.random.Generator(PCG64(seed)); draw order is pool, slots,
   then q, k, v, g, beta (per decode step, or once per prefill batch).
+* Raw (un-normalised) q and k, for the cases that exercise the kernels' own
+  L2 normalisation: instead of normalising, every (token, key head) row of q
+  and of k is rescaled to a norm drawn log-uniformly in [lo, hi] (one extra
+  draw per tensor, after beta), and the rows with (t + j) % 11 == 3 (k) or
+  (t + j) % 13 == 5 (q), t the token and j the key head, get norm 1e-4, where
+  the normalisation's epsilon dominates.
 """
 
 from __future__ import annotations
@@ -58,8 +64,22 @@ class Tokens:
     beta: np.ndarray       # [T, HV]
 
 
+TINY_ROW_NORM = 1e-4
+
+
+def _rescale_rows(rng, x, lo, hi, tiny_mod, tiny_rem):
+    """Rows of x [T, HK, d] rescaled to norms log-uniform in [lo, hi]; rows
+    with (t + j) % tiny_mod == tiny_rem to norm TINY_ROW_NORM."""
+    T, HK, _ = x.shape
+    target = np.exp(rng.uniform(np.log(lo), np.log(hi), size=(T, HK))).astype(np.float32)
+    tt, jj = np.meshgrid(np.arange(T), np.arange(HK), indexing="ij")
+    target[(tt + jj) % tiny_mod == tiny_rem] = np.float32(TINY_ROW_NORM)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32))
+    return (x / n * target[..., None]).astype(np.float32)
+
+
 def draw_tokens(rng, T, HK, HV, dk, dv, dtype, *, g_range=(0.01, 0.5),
-                beta_mode="sigmoid", normalise_qk=True, v_scale=1.0) -> Tokens:
+                beta_mode="sigmoid", normalise_qk=True, v_scale=1.0, raw_norms=None) -> Tokens:
     q = rng.standard_normal((T, HK, dk), dtype=np.float32)
     k = rng.standard_normal((T, HK, dk), dtype=np.float32)
     v = (rng.standard_normal((T, HV, dv), dtype=np.float32) * np.float32(v_scale)).astype(np.float32)
@@ -69,7 +89,12 @@ def draw_tokens(rng, T, HK, HV, dk, dv, dtype, *, g_range=(0.01, 0.5),
         beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, HV))))).astype(np.float32)
     else:
         beta = np.full((T, HV), float(beta_mode), np.float32)
-    if normalise_qk:
+    if raw_norms is not None:
+        if normalise_qk:
+            raise ValueError("raw_norms needs normalise_qk=False")
+        q = _rescale_rows(rng, q, raw_norms[0], raw_norms[1], 13, 5)
+        k = _rescale_rows(rng, k, raw_norms[0], raw_norms[1], 11, 3)
+    elif normalise_qk:
         q = _normalise_rows_f32(q)
         k = _normalise_rows_f32(k)
     if dtype == BF16:
@@ -129,30 +154,33 @@ class VerifyWorkload:
 
 
 def verify_workload(name, *, seed, B, K, HK, HV, dk, dv, dtype, num_slots, pool_sigma,
-                    src=None, g_range=(0.01, 0.5), beta_mode="sigmoid") -> VerifyWorkload:
+                    src=None, g_range=(0.01, 0.5), beta_mode="sigmoid", raw_norms=None) -> VerifyWorkload:
     rng = np.random.Generator(np.random.PCG64(seed))
     pool = (rng.standard_normal((num_slots, HV, dk, dv), dtype=np.float32) * np.float32(pool_sigma)).astype(np.float32)
     if src is None:
         src = rng.permutation(num_slots)[:B]
     src = np.asarray(src, np.int32)
-    toks = draw_tokens(rng, B * K, HK, HV, dk, dv, dtype, g_range=g_range, beta_mode=beta_mode)
+    toks = draw_tokens(rng, B * K, HK, HV, dk, dv, dtype, g_range=g_range, beta_mode=beta_mode,
+                       normalise_qk=raw_norms is None, raw_norms=raw_norms)
     return VerifyWorkload(name, B, K, HK, HV, dk, dv, dtype, num_slots, pool, src, toks)
 
 
 def decode_workload(name, *, seed, B, HK, HV, dk, dv, dtype, num_slots, pool_sigma,
-                    steps, src=None, g_range=(0.01, 0.5), beta_mode="sigmoid") -> DecodeWorkload:
+                    steps, src=None, g_range=(0.01, 0.5), beta_mode="sigmoid", raw_norms=None) -> DecodeWorkload:
     rng = np.random.Generator(np.random.PCG64(seed))
     pool = (rng.standard_normal((num_slots, HV, dk, dv), dtype=np.float32) * np.float32(pool_sigma)).astype(np.float32)
     if src is None:
         src = rng.permutation(num_slots)[:B]
     src = np.asarray(src, np.int32)
-    toks = [draw_tokens(rng, B, HK, HV, dk, dv, dtype, g_range=g_range, beta_mode=beta_mode)
+    toks = [draw_tokens(rng, B, HK, HV, dk, dv, dtype, g_range=g_range, beta_mode=beta_mode,
+                        normalise_qk=raw_norms is None, raw_norms=raw_norms)
             for _ in range(steps)]
     return DecodeWorkload(name, B, HK, HV, dk, dv, dtype, num_slots, pool, src, toks)
 
 
 def prefill_workload(name, *, seed, lengths, HK, HV, dk, dv, dtype, num_slots, pool_sigma=0.0,
-                     src=None, g_range=(0.01, 0.5), beta_mode="sigmoid", v_scale=1.0) -> PrefillWorkload:
+                     src=None, g_range=(0.01, 0.5), beta_mode="sigmoid", v_scale=1.0,
+                     raw_norms=None) -> PrefillWorkload:
     rng = np.random.Generator(np.random.PCG64(seed))
     if pool_sigma > 0:
         pool = (rng.standard_normal((num_slots, HV, dk, dv), dtype=np.float32) * np.float32(pool_sigma)).astype(np.float32)
@@ -165,7 +193,8 @@ def prefill_workload(name, *, seed, lengths, HK, HV, dk, dv, dtype, num_slots, p
         src = -np.ones(N, np.int32)
     src = np.asarray(src, np.int32)
     toks = draw_tokens(rng, int(cu[-1]), HK, HV, dk, dv, dtype, g_range=g_range,
-                       beta_mode=beta_mode, v_scale=v_scale)
+                       beta_mode=beta_mode, v_scale=v_scale, normalise_qk=raw_norms is None,
+                       raw_norms=raw_norms)
     return PrefillWorkload(name, HK, HV, dk, dv, dtype, num_slots, pool, cu, src, toks)
 
 
@@ -216,12 +245,17 @@ def long_packed_lengths(first=50_000, n_short=16, lo=1024, hi=16384, seed=4) -> 
     return [first] + [int(x) for x in rng.integers(lo, hi, size=n_short, endpoint=True)]
 
 
-def long_packed_prefill(first=50_000, n_short=16, lo=1024, hi=16384, seed=4) -> PrefillWorkload:
+def long_packed_prefill(first=50_000, n_short=16, lo=1024, hi=16384, seed=4,
+                        g_range=(0.01, 0.5)) -> PrefillWorkload:
     """One 50,000-token sequence plus 16 sequences with lengths uniform in
-    [1024, 16384] (inclusive), packed via cu_seqlens, zero initial states."""
+    [1024, 16384] (inclusive), packed via cu_seqlens, zero initial states.
+    ``g_range`` other than the default gives a weak-decay variant of the same
+    shape (the lengths do not change)."""
     lengths = long_packed_lengths(first, n_short, lo, hi, seed)
-    return prefill_workload("long_packed_prefill_bf16_h32_128x128", seed=seed + 100, lengths=lengths,
-                            HK=16, HV=32, dk=128, dv=128, dtype=BF16, num_slots=len(lengths) + 1)
+    name = "long_packed_prefill_bf16_h32_128x128" + ("" if tuple(g_range) == (0.01, 0.5) else "_weak_decay")
+    return prefill_workload(name, seed=seed + 100, lengths=lengths,
+                            HK=16, HV=32, dk=128, dv=128, dtype=BF16, num_slots=len(lengths) + 1,
+                            g_range=g_range)
 
 
 def spec_verify(B=64, K=4) -> VerifyWorkload:

@@ -237,29 +237,45 @@ def test_multiturn_resume_from_shared_checkpoints():
     pool.close()
 
 
-def test_long_packed_prefill_sampled():
-    """50,000 + 16 x U[1K, 16K] tokens packed (about 190K tokens). All runs on
-    the GPU; the oracle checks value heads 0, 1 of the first 4096 tokens of
-    the long sequence (outputs depend only on earlier tokens) and the full
-    state of the shortest packed sequence."""
-    pw = long_packed_prefill()
+@pytest.mark.parametrize("variant", ["default_decay", "weak_decay"])
+def test_long_packed_prefill_sampled(variant):
+    """50,000 + 16 x U[1K, 16K] tokens packed (about 219K tokens), all on the
+    GPU in one call. The planner cuts the 50,000-token sequence into three
+    segments of 261 chunks (tokens [0, 16704), [16704, 33408), [33408,
+    50000)), so the later two start from chained segment states. The oracle
+    follows value heads 0, 1 (key head 0) through the whole long sequence:
+    every output of all three segments and the final state are compared; for
+    the weak-decay variant (g = -U(1e-4, 1e-2), so the state carried across
+    segment boundaries shapes the outputs) also value heads 30, 31 (key head
+    15). The shortest packed sequence is compared in full on heads 0, 1."""
+    import sys
+    g_range = (0.01, 0.5) if variant == "default_decay" else (1e-4, 1e-2)
+    pw = long_packed_prefill(g_range=g_range)
     N = len(pw.cu_seqlens) - 1
     src = [-1] * N
     dst = list(range(N))
     o, st, _ = _gpu_prefill(pw, src, dst)
     og = out_f64(o)
+    got = st.cpu().numpy()
     tk = pw.tokens
     cu = pw.cu_seqlens
-    heads = [0, 1]
-    o_ref, _ = recurrent_sequence(np.zeros((2, 128, 128)), as_f64(tk.q[:4096, :1], BF16), as_f64(tk.k[:4096, :1], BF16),
-                                  as_f64(tk.v[:4096, :2], BF16), tk.g[:4096, :2], tk.beta[:4096, :2], 128 ** -0.5, EPS)
-    check_outputs(og[:4096, heads], o_ref, BF16, "long sequence head")
+    L = int(cu[1])
+    groups = [(0, [0, 1])] if variant == "default_decay" else [(0, [0, 1]), (15, [30, 31])]
+    for kh, heads in groups:
+        print(f"[cfg4 {variant}] oracle over {L} tokens, heads {heads}", file=sys.stderr, flush=True)
+        o_ref, h_ref = recurrent_sequence(np.zeros((2, 128, 128)), as_f64(tk.q[:L, kh:kh + 1], BF16),
+                                          as_f64(tk.k[:L, kh:kh + 1], BF16), as_f64(tk.v[:L, heads], BF16),
+                                          tk.g[:L, heads], tk.beta[:L, heads], 128 ** -0.5, EPS)
+        for a, b in ((0, 16704), (16704, 33408), (33408, L)):
+            check_outputs(og[a:b, heads], o_ref[a:b], BF16, f"long sequence heads {heads} tokens [{a}, {b})")
+        check_state(got[0][heads], h_ref, BF16, f"long sequence final state heads {heads}")
     n = int(np.argmin(np.diff(cu)[1:])) + 1
     a, b = cu[n], cu[n + 1]
+    heads = [0, 1]
     o_ref, h_ref = recurrent_sequence(np.zeros((2, 128, 128)), as_f64(tk.q[a:b, :1], BF16), as_f64(tk.k[a:b, :1], BF16),
                                       as_f64(tk.v[a:b, :2], BF16), tk.g[a:b, :2], tk.beta[a:b, :2], 128 ** -0.5, EPS)
     check_outputs(og[a:b, heads], o_ref, BF16, f"seq {n}")
-    check_state(st[n].cpu().numpy()[heads], h_ref, BF16, f"seq {n} state")
+    check_state(got[n][heads], h_ref, BF16, f"seq {n} state")
 
 
 # --- long sequences cut into segments (pass 1: segment end states and
