@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
 SOURCES = ["gdn_pool.cpp", "gdn_abi.cpp", "gdn_prefix_cache.cpp", "gdn_decode.hip", "gdn_prefill.hip",
-           "gdn_transfer.hip", "gdn_graph.hip", "gdn_prefill_f32.hip"]
+           "gdn_transfer.hip", "gdn_graph.hip", "gdn_prefill_f32.hip", "gdn_static_ws.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

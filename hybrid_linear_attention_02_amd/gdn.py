@@ -43,7 +43,10 @@ EXPORTED = (
     "gdn_prefix_cache_match", "gdn_prefix_cache_evict", "gdn_prefix_cache_size",
     "gdn_decode_graph_create", "gdn_decode_graph_launch", "gdn_decode_graph_poll",
     "gdn_decode_graph_wait_entry", "gdn_decode_graph_sync_entry", "gdn_decode_graph_destroy",
+    "gdn_prefill_chunked_static",
 )
+
+GDN_PREFILL_STATIC_WORKSPACE_BYTES = 64 << 20
 
 GDN_GRAPH_LAYER_EVENTS = 1
 GDN_GRAPH_MAX_ENTRIES = 4096
@@ -124,6 +127,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gdn_decode_verify": ([P, POINTER(VerifyArgs), P], c_int32),
         "gdn_prefill_workspace_bytes": ([P, POINTER(PrefillArgs), POINTER(c_size_t)], c_int32),
         "gdn_prefill_chunked": ([P, POINTER(PrefillArgs), P, c_size_t, P], c_int32),
+        "gdn_prefill_chunked_static": ([P, POINTER(PrefillArgs), P], c_int32),
         "gdn_decode_graph_create": ([P, c_int32, POINTER(DecodeArgs), POINTER(P), c_int32, POINTER(P)], c_int32),
         "gdn_decode_graph_launch": ([P, P], c_int32),
         "gdn_decode_graph_poll": ([P, POINTER(ctypes.c_uint32), POINTER(c_int32)], c_int32),
@@ -601,3 +605,16 @@ def gdn_prefill_chunked(pool: StatePool, q, k, v, g, beta, o, cu_seqlens, cu_seq
         # that stream's work ends
         workspace.record_stream(stream)
     return workspace
+
+
+def gdn_prefill_chunked_static(pool: StatePool, q, k, v, g, beta, o, cu_seqlens, cu_seqlens_host, src_slots,
+                               dst_slots, *, scale=None, l2_eps: float = 1e-6, err_flag=None, ckpt_slots=None,
+                               stream=None) -> None:
+    """gdn_prefill_chunked on the library's static per-GPU workspace (no
+    device allocation anywhere, here or in the library). Same arguments and
+    results; calls needing more than GDN_PREFILL_STATIC_WORKSPACE_BYTES of
+    workspace raise. Calls whose work overlaps on one GPU share that workspace
+    and must be serialised by the caller."""
+    a, host = _prefill_args(pool, q, k, v, g, beta, o, cu_seqlens, cu_seqlens_host, src_slots, dst_slots,
+                            scale, l2_eps, err_flag, ckpt_slots)
+    _check(load_library().gdn_prefill_chunked_static(c_void_p(pool.handle), byref(a), _stream(stream)))

@@ -372,6 +372,24 @@ int gdn_prefill_workspace_bytes(const gdn_pool* pool, const gdn_prefill_args* ar
 int gdn_prefill_chunked(const gdn_pool* pool, const gdn_prefill_args* args, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* The same prefill for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Identical arguments and results to gdn_prefill_chunked, but the
+ * workspace is a file-scope device array inside the library, one per GPU,
+ * GDN_PREFILL_STATIC_WORKSPACE_BYTES (64 MiB) long, held until the process
+ * ends. The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); on its first use on a GPU it looks up that GPU's copy of
+ * the array once. A call whose workspace (gdn_prefill_workspace_bytes)
+ * exceeds the array returns GDN_E_INVALID and enqueues nothing: 64 MiB covers
+ * one 4096-token call at 16 key / 32 value heads of 128 x 128 (52.5 MiB),
+ * and every call of fp32 inputs (whose workspace holds only offsets). The workspace needs no clearing
+ * between calls. Every call on one GPU shares that GPU's array: two calls
+ * whose work overlaps on one GPU (different streams, or graphs replayed
+ * concurrently) race on it and must be serialised by the caller. The device
+ * is the stream's (the current device for the NULL stream). */
+#define GDN_PREFILL_STATIC_WORKSPACE_BYTES (64u << 20)
+int gdn_prefill_chunked_static(const gdn_pool* pool, const gdn_prefill_args* args, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* gdn_last_error(void);
 
