@@ -3,11 +3,15 @@
 Primary line: batched decode -- 64 requests, 16 key / 32 value heads, 128 x 128
 fp32 state tiles in a 256-slot pool, bf16 q/k/v -- one step = one
 gdn_decode_step over the batch (slot resolution, normalisation, decay, delta
-write, read-out, state store). The first timed step reads the source slots and
-writes fresh destination slots; later steps update those in place. The K timed
-steps are recorded once as a HIP graph and replayed, as the engine on the
-TokenSpeed pages records its decode loop. `value` is algorithmic bytes per
-second over the K timed steps (inputs resident in HBM).
+write, read-out, state store). The K timed steps rotate over 4 GDN layers, each
+with its own pool of the workload; a layer's first step reads the source slots
+and writes fresh destination slots, its later steps update those in place, and
+between two of its steps the other layers stream 768 MiB, so its state comes
+from HBM, not the 256 MB MALL. The K steps are recorded once as a HIP graph and
+replayed, as the engine on the TokenSpeed pages records its decode loop.
+`value` is algorithmic bytes per second over the K timed steps (inputs
+resident in HBM); a decode-shaped tile copy on the same protocol is reported
+beside it as the measured ceiling.
 
 Also measured in the same run (the metric has two halves):
   * chunked prefill of one 8192-token bf16 sequence (same head shape), reported
@@ -96,12 +100,50 @@ def _traffic(profile_name, src_names, launches_bytes_key):
         return None
 
 
-def bench_decode(steps, warmup):
-    """Batched decode. The K timed steps are recorded once as a HIP graph and
-    replayed (the engine on the pages records its whole decode loop as one
-    graph); `value` and the roofline use the replay's span on the stream the
-    kernels run on. Eager per-launch times and a cold-cache figure are
-    reported beside it."""
+DECODE_LAYERS = 4   # GDN layers the timed decode steps rotate over (HBM-only protocol)
+
+
+def _decode_layers(wl, layers):
+    """`layers` GDN layers of the batched workload, each its own 256-slot pool
+    (the same initial tiles and slot tables): sources hold checkpoints,
+    destinations come off the free list."""
+    import torch
+    from hybrid_linear_attention_02_amd import gdn
+    init = torch.from_numpy(np.ascontiguousarray(wl.pool)).cuda()
+    pools = []
+    dst = None
+    for _ in range(layers):
+        pool = gdn.gdn_state_pool_create(wl.num_slots, wl.HV, wl.dk, wl.dv, storage=init.clone())
+        pool.alloc(wl.num_slots)
+        keep = set(int(s) for s in wl.src)
+        for s in range(wl.num_slots):
+            if s not in keep:
+                pool.release(s)
+        d = pool.alloc(wl.B)
+        pool.validate(list(wl.src), d)
+        assert dst is None or d == dst
+        dst = d
+        pools.append(pool)
+    return init, pools, dst
+
+
+def bench_decode(steps, warmup, layers=DECODE_LAYERS):
+    """Batched decode, HBM-only protocol (``value`` and the roofline).
+
+    Every timed step is one gdn_decode_step of the batched workload (64
+    requests, 16/32 heads, 128 x 128 fp32 tiles in a 256-slot pool, bf16
+    inputs). The K steps rotate over `layers` GDN layers, each with its own
+    pool: step s updates layer s % layers, whose first step reads the source
+    checkpoints and writes fresh slots and whose later steps update those in
+    place. Between two steps of a layer the other layers read and write
+    3 x 256 MiB, so the 256 MB MALL holds none of that layer's 128 MiB of
+    state: the steps stream HBM, as a decode step does in a model whose other
+    layers run in between. The K steps are recorded once as a HIP graph (the
+    engine on the pages records its decode loop) and replayed.
+
+    Reported beside it: the same K steps on one layer (in place, whose 128
+    MiB working set the MALL can hold: warm), eager launches, and single
+    launches after a 1 GiB device write (cold)."""
     import torch
     from hybrid_linear_attention_02_amd import gdn
     from hybrid_linear_attention_02_amd.workloads import batched_decode
@@ -110,62 +152,63 @@ def bench_decode(steps, warmup):
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
     inputs = [(bf(t.q), bf(t.k), bf(t.v), dev(t.g), dev(t.beta)) for t in wl.steps]
-    init = dev(wl.pool)
-    storage = init.clone()
-    pool = gdn.gdn_state_pool_create(wl.num_slots, wl.HV, wl.dk, wl.dv, storage=storage)
-    # sources hold checkpoints; destinations come off the free list
-    pool.alloc(wl.num_slots)
-    keep = set(int(s) for s in wl.src)
-    for s in range(wl.num_slots):
-        if s not in keep:
-            pool.release(s)
-    dst = pool.alloc(wl.B)
-    pool.validate(list(wl.src), dst)
+    init, pools, dst = _decode_layers(wl, layers)
     src_t = torch.tensor(wl.src, dtype=torch.int32, device="cuda")
     dst_t = torch.tensor(dst, dtype=torch.int32, device="cuda")
     o = torch.empty((wl.B, wl.HV, wl.dv), dtype=torch.bfloat16, device="cuda")
     per_req = decode_bytes_per_request(wl.HK, wl.HV, wl.dk, wl.dv, 2)
     bytes_step = wl.B * per_req
+    stream = torch.cuda.current_stream()
 
-    def step(i, first):
+    def step(pool, i, first):
         q, k, v, g, b = inputs[i]
         gdn.gdn_decode_step(pool, q, k, v, g, b, o, src_t if first else dst_t, dst_t)
 
+    def reset():
+        for p in pools:
+            p.storage.copy_(init)
+        torch.cuda.synchronize()
+
     for i in range(warmup):
-        step(steps + i, i == 0)
+        step(pools[i % layers], steps + i, i < layers)
     torch.cuda.synchronize()
 
-    # record the K steps: step 0 reads the checkpoints, later steps update in place
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=side):
-        for i in range(steps):
-            step(i, i == 0)
-    torch.cuda.synchronize()
+    def record(n_layers):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(steps):
+                step(pools[i % n_layers], i, i < n_layers)
+        torch.cuda.synchronize()
+        return graph
 
-    stream = torch.cuda.current_stream()
-    storage.copy_(init)                       # timed run starts from the initial pool
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    graph.replay()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    span_ms = ev0.elapsed_time(ev1)
+    def replay(graph):
+        reset()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1), time.perf_counter() - t0
+
+    g_rot = record(layers)
+    span_ms, wall = replay(g_rot)
     value = bytes_step * steps / (span_ms * 1e-3) / 1e9
     launch_ms = span_ms / steps               # average launch duration inside the replay
     achieved = bytes_step / (launch_ms * 1e-3) / 1e9
+    del g_rot
+    g_one = record(1)
+    warm_ms, _ = replay(g_one)
+    del g_one
 
-    # eager launches, each bracketed by its own events (Python launch gaps included in the span)
-    storage.copy_(init)
-    torch.cuda.synchronize()
+    # eager launches on the rotating layers, each bracketed by its own events
+    reset()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record(stream)
-        step(i, i == 0)
+        step(pools[i % layers], i, i < layers)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     eager_ms = np.array([a.elapsed_time(b) for a, b in ev])
@@ -174,20 +217,40 @@ def bench_decode(steps, warmup):
     # cold-cache figure: each launch preceded by a 1 GiB write (outside the events)
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     cold = []
-    for i in range(min(steps, 20)):
+    for i in range(20):
         flush.fill_(float(i))
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        step(i, False)
+        step(pools[0], i, False)
         b.record(stream)
         torch.cuda.synchronize()
         cold.append(a.elapsed_time(b))
-    del flush, graph
+    del flush
     cold_gbs = bytes_step / (float(np.median(cold)) * 1e-3) / 1e9
+
+    # decode-shaped copy on the same protocol: the library's tile gather
+    # (gdn_state_pool_pack: one workgroup per 64 KiB tile, 128-bit
+    # non-temporal loads and stores, as the decode kernel streams its tiles)
+    # of the same 64 slots x 32 heads per step, rotating over the layers
+    # into one buffer per layer: 128 MiB read + 128 MiB written per step
+    bufs = [torch.empty((wl.B, wl.HV, wl.dk, wl.dv), dtype=torch.float32, device="cuda") for _ in range(layers)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g_copy = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_copy, stream=side):
+        for i in range(steps):
+            gdn.gdn_state_pool_pack(pools[i % layers], dst_t, bufs[i % layers])
+    torch.cuda.synchronize()
+    copy_ms, _ = replay(g_copy)
+    copy_bytes = 2 * wl.B * wl.HV * wl.dk * wl.dv * 4
+    copy_gbs = copy_bytes * steps / (copy_ms * 1e-3) / 1e9
+    del g_copy, bufs
     traffic = _traffic("decode_counters_batched_b64_h32_128x128.txt", ["gdn_decode.hip"], "hbm_bytes_per_launch")
-    pool.close()
+    for p in pools:
+        p.close()
     return dict(
         value=value, ms_per_step=span_ms / steps, wall_s=wall, achieved=achieved, cold_gbs=cold_gbs,
+        warm_gbs=bytes_step * steps / (warm_ms * 1e-3) / 1e9, tile_copy_gbs=copy_gbs, layers=layers,
         bytes_step=bytes_step, per_req=per_req, B=wl.B, HK=wl.HK, HV=wl.HV, dk=wl.dk, dv=wl.dv,
         launch_ms_mean=launch_ms, traffic=traffic,
         eager={"launch_us_mean": float(eager_ms.mean() * 1e3), "launch_us_median": float(np.median(eager_ms) * 1e3),
@@ -976,17 +1039,26 @@ def main():
             "workload": "batched_decode_bf16_b64_hk16_hv32_128x128_pool256",
             "requests": d["B"], "k_heads": d["HK"], "v_heads": d["HV"], "dk": d["dk"], "dv": d["dv"],
             "io_dtype": "bf16", "state_dtype": "f32", "pool_slots": 256,
-            "bytes_per_step": d["bytes_step"],
+            "bytes_per_step": d["bytes_step"], "layers_rotated": d["layers"],
         },
         "hbm_frac": round(d["value"] / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(d["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(d["achieved"] / HBM_PEAK_GBS, 4), "traffic": d["traffic"],
             "kernel": "gdn_decode_kernel<128,128,128,bf16> (whole tiles)", "launch_us_mean": round(d["launch_ms_mean"] * 1e3, 2),
-            "timing": "HIP-graph replay of the K timed steps; achieved = bytes per launch / (replay span / K)",
-            "note": "the 64 requests' 128 MiB of state fits the 256 MB MALL, so in-place steps after the first "
-                    "may be served partly from it; cold_cache is the HBM-only figure",
+            "timing": f"HIP-graph replay of the K timed steps rotating over {d['layers']} layers' pools "
+                      "(HBM-only: the MALL holds none of a layer's state between its steps); "
+                      "achieved = bytes per launch / (replay span / K)",
+            "vs_tile_copy": round(d["achieved"] / d["tile_copy_gbs"], 4),
         },
+        "decode_shaped_copy": {"value": round(d["tile_copy_gbs"], 1), "unit": "GB/s",
+                               "frac": round(d["tile_copy_gbs"] / HBM_PEAK_GBS, 4),
+                               "protocol": "gdn_state_pool_pack of the same 64 slots x 32 heads per step (one "
+                                           "workgroup per 64 KiB tile, read then written), K steps rotating over "
+                                           "the same layers, one HIP-graph replay"},
+        "warm_one_layer": {"value": round(d["warm_gbs"], 1), "unit": "GB/s", "frac": round(d["warm_gbs"] / HBM_PEAK_GBS, 4),
+                           "protocol": "the K steps on one layer in place (128 MiB working set, which the 256 MB "
+                                       "MALL can hold), one HIP-graph replay"},
         "eager": {k: round(v, 2) for k, v in d["eager"].items()},
         "cold_cache": {"value": round(d["cold_gbs"], 1), "unit": "GB/s", "frac": round(d["cold_gbs"] / HBM_PEAK_GBS, 4),
                        "protocol": "median of 20 single launches, each after a 1 GiB device write"},
