@@ -102,6 +102,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"libgdn.so not found at {path}; build it first "
             "(python -m hybrid_linear_attention_02_amd.build or __graft_entry__.build())")
+    # One HIP runtime per process: torch carries its own libamdhip64 (soname
+    # libamdhip64.so.7, which its libraries request by file name), and
+    # libgdn.so binds to whichever libamdhip64.so.7 is loaded first. Loading
+    # torch first makes the library use torch's runtime, so the tensors,
+    # streams and graphs torch hands over are that runtime's own. Opened the
+    # other way round, the process would hold two runtimes.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = c_void_p
     sig = {

@@ -60,3 +60,20 @@ def test_prefill_binding_consistent_host_tensors_reach_the_device_check():
     with pytest.raises(ValueError, match="device tensor"):
         gdn.gdn_prefill_chunked(None, a["q"], a["k"], a["v"], a["g"], a["beta"], a["o"], a["cu_seqlens"],
                                 a["cu_seqlens_host"], a["src_slots"], a["dst_slots"])
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library first must not put a second HIP runtime into the
+    process: in a fresh interpreter that opens libgdn.so before anything
+    else, exactly one libamdhip64 is mapped, and it is torch's."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("from hybrid_linear_attention_02_amd import gdn; gdn.load_library(); "
+            "print('\\n'.join(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l})))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    libs = out.stdout.split()
+    import torch
+    assert libs == [os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")], libs
