@@ -127,7 +127,7 @@ extern "C" int gdn_prefill_workspace_bytes(const gdn_pool* pool, const gdn_prefi
 namespace gdn {
 
 static bool prefill_dims_supported(int32_t dk, int32_t dv) {
-    return (dk == 32 || dk == 64 || dk == 128) && (dv == 16 || dv == 32 || dv == 64 || dv == 128);
+    return (dk == 16 || dk == 32 || dk == 64 || dk == 128) && (dv == 16 || dv == 32 || dv == 64 || dv == 128);
 }
 
 // Segment length of the sequence split, from a cost model of the three
@@ -141,8 +141,10 @@ static bool prefill_dims_supported(int32_t dk, int32_t dv) {
 // (no split) when one pass is estimated fastest.
 int32_t choose_seg_len(const int32_t* cu, int32_t n, int32_t hv, int32_t dk, int32_t dv) {
     constexpr double kState = 2800, kOut = 3800, kHop = 6000;
-    const int64_t w_out = static_cast<int64_t>(hv) * (dv / 64);          // workgroups per segment, output pass
-    const int64_t w_state = static_cast<int64_t>(hv) * (dv / 64 + dk / 64);  // state pass
+    const int nvo = 16 * prefill_output_waves(dv), nvs = 16 * prefill_state_waves(dk, dv);
+    const int64_t w_out = static_cast<int64_t>(hv) * (dv / nvo);               // workgroups per segment, output pass
+    const int64_t w_val = static_cast<int64_t>(hv) * (dv / nvs);               // state pass, first segment
+    const int64_t w_state = static_cast<int64_t>(hv) * ((dv + dk) / nvs);      // state pass, later segments
     auto pass = [](int64_t wg_steps, int64_t longest) {
         // whole rounds of kNumCUs workgroups, each at least `longest` steps
         const double rounds = std::ceil(static_cast<double>(wg_steps) / (static_cast<double>(kNumCUs) * longest));
@@ -156,7 +158,7 @@ int32_t choose_seg_len(const int32_t* cu, int32_t n, int32_t hv, int32_t dk, int
             const int64_t nseg = (L == 0 || c <= L) ? 1 : (c + L - 1) / L;
             const int64_t seg = (nseg == 1) ? c : L;
             out_steps += (c + nseg) * w_out;
-            if (nseg > 1) state_steps += L * w_out + (nseg - 2) * L * w_state;
+            if (nseg > 1) state_steps += L * w_val + (nseg - 2) * L * w_state;
             longest = std::max(longest, seg + 1);
             hops = std::max(hops, nseg - 1);
         }
@@ -194,7 +196,7 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     if (a->dtype != GDN_DTYPE_BF16 && !f32)
         return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: dtype must be GDN_DTYPE_BF16 or GDN_DTYPE_F32");
     if (!f32 && !prefill_dims_supported(a->dk, a->dv))
-        return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: dk must be 32, 64 or 128 and dv 16, 32, 64 or 128");
+        return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: dk and dv must be 16, 32, 64 or 128");
     if (!std::isfinite(a->scale) || !(a->l2_eps >= 0.0f) || !std::isfinite(a->l2_eps))
         return fail(GDN_E_INVALID, "gdn_prefill_chunked: scale must be finite and l2_eps finite and >= 0");
     const int32_t n = a->num_seqs;
@@ -218,9 +220,9 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     if (chunks * a->num_v_heads > INT32_MAX / 2)
         return fail(GDN_E_INVALID, "gdn_prefill_chunked: too many chunks");
     plan->num_chunks = static_cast<int32_t>(chunks);
-    // (the transition columns and the transition products work in 64-column groups)
-    const bool can_split = !f32 && a->dk >= 64 && a->dv >= 64;
-    plan->seg_len = can_split ? choose_seg_len(a->cu_seqlens_host, n, a->num_v_heads, a->dk, a->dv) : 0;
+    const bool can_split = !f32;
+    const int32_t kdk = f32 ? a->dk : prefill_kernel_dk(a->dk);   // the kernels' dk (workspace tiles)
+    plan->seg_len = can_split ? choose_seg_len(a->cu_seqlens_host, n, a->num_v_heads, kdk, a->dv) : 0;
     int64_t segs = 0;
     for (int32_t i = 0; i < n; ++i) {
         const int64_t c = (static_cast<int64_t>(a->cu_seqlens_host[i + 1]) - a->cu_seqlens_host[i] + 63) / 64;
@@ -229,7 +231,7 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     if (segs > 65535) return fail(GDN_E_INVALID, "gdn_prefill_chunked: too many sequence segments");
     plan->num_segs = static_cast<int32_t>(segs);
     const bool split = plan->seg_len > 0;
-    const size_t hv = static_cast<size_t>(a->num_v_heads), dk = static_cast<size_t>(a->dk), dv = static_cast<size_t>(a->dv);
+    const size_t hv = static_cast<size_t>(a->num_v_heads), dk = static_cast<size_t>(kdk), dv = static_cast<size_t>(a->dv);
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     size_t off = 0;
     plan->off_chunk_offsets = off;

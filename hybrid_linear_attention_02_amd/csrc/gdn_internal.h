@@ -46,6 +46,19 @@ int launch_transfer(const gdn_pool* pool, bool pack, int32_t n, const int32_t* s
 constexpr int kNumCUs = 256;      // MI355X compute units
 int32_t choose_seg_len(const int32_t* cu_host, int32_t n, int32_t hv, int32_t dk, int32_t dv);
 
+// Compute waves (16 value columns each) per workgroup of the bf16
+// recurrence: the output pass takes min(dv, 64) columns per workgroup, the
+// state pass at most dk of them, so that its dk transition columns split
+// into whole groups too.
+inline int prefill_output_waves(int dv) { return dv >= 64 ? 4 : dv / 16; }
+// dk the bf16 prefill kernels run at: dk = 16 runs at 32 (the MFMA k-step),
+// with q and k zero-padded and the pool tiles' 16 rows read and written only.
+inline int prefill_kernel_dk(int dk) { return dk < 32 ? 32 : dk; }
+inline int prefill_state_waves(int dk, int dv) {
+    const int nw = prefill_output_waves(dv);
+    return nw * 16 <= dk ? nw : dk / 16;
+}
+
 struct PrefillPlan {
     int32_t num_chunks = 0;       // sum over sequences of ceil(len / 64)
     int32_t seg_len = 0;          // chunks per segment, 0 = no split (one segment per sequence)

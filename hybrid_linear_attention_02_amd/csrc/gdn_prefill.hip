@@ -99,6 +99,8 @@ struct PrefillParams {
     int32_t hk;
     int32_t hv;
     int32_t group;
+    int32_t dkq;                // dk of q, k and the pool tiles; the kernels run at DK >= dkq
+                                // (dk = 16 runs at DK = 32 with zero-padded rows and columns)
     int32_t dv;
     int32_t num_slots;
     float scale;
@@ -433,10 +435,11 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     // global round trip, not five.
     const auto load_rows = [&](const uint16_t* x, int tt, u32x4* dst) {
         const int r = 16 * tt + l16;
-        const size_t base = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + 8 * g4;
+        const size_t base = (static_cast<size_t>(t0 + r) * p.hk + j) * p.dkq + 8 * g4;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            dst[ks] = (r < len) ? *reinterpret_cast<const u32x4*>(x + base + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+            dst[ks] = (r < len && 32 * ks + 8 * g4 < p.dkq) ? *reinterpret_cast<const u32x4*>(x + base + 32 * ks)
+                                                             : u32x4{0u, 0u, 0u, 0u};
     };
     // sum of squares of the row held in operand layout, over all four lane groups
     const auto row_sumsq = [&](const u32x4* xr) {
@@ -811,7 +814,7 @@ prefill_recurrent_kernel(PrefillParams p) {
     // into the segment, and rows past a chunk's end or a disabled store fall
     // outside a buffer resource's range, where loads return zero and stores
     // are dropped.
-    const unsigned kq_row = static_cast<unsigned>(p.hk) * DK;   // elements between token rows
+    const unsigned kq_row = static_cast<unsigned>(p.hk) * p.dkq;   // elements between token rows
     const unsigned v_row = static_cast<unsigned>(p.hv) * p.dv;
     const int htid = tid - NA;
     constexpr unsigned kOff = 0x80000000u;      // offset past every range
@@ -820,12 +823,12 @@ prefill_recurrent_kernel(PrefillParams p) {
     auto fetch = [&](int c) {
         const int t0 = tb + (c - c0) * kC;
         const int len = chunk_len(c);
-        const rsrc_t kr = make_rsrc(p.k + (static_cast<size_t>(t0) * p.hk + j) * DK, rows_bytes(len, kq_row, DK));
+        const rsrc_t kr = make_rsrc(p.k + (static_cast<size_t>(t0) * p.hk + j) * p.dkq, rows_bytes(len, kq_row, p.dkq));
 #pragma unroll
         for (int m = 0; m < KQ; ++m) {
             const int idx = htid + S::NB * m;
             const int r = idx / (DK / 8), c8 = idx % (DK / 8);
-            rK[m] = buf_load16(kr, 2u * (r * kq_row + c8 * 8));
+            rK[m] = buf_load16(kr, 8 * c8 < p.dkq ? 2u * (r * kq_row + c8 * 8) : kOff);   // padded columns: zero
         }
         // T fragments; the two all-zero ones, (0, 1) and (1, 1), are never
         // written by the intra-chunk kernel nor read here (they load as zero)
@@ -885,10 +888,12 @@ prefill_recurrent_kernel(PrefillParams p) {
     // kilobyte per (row tile, k-step)
     auto fetch_rows = [&](int c, HelperRows<KS>& hr) {
         const int t0 = tb + (c - c0) * kC;
-        const rsrc_t qr = make_rsrc(p.q + (static_cast<size_t>(t0) * p.hk + j) * DK, rows_bytes(chunk_len(c), kq_row, DK));
+        const rsrc_t qr = make_rsrc(p.q + (static_cast<size_t>(t0) * p.hk + j) * p.dkq, rows_bytes(chunk_len(c), kq_row, p.dkq));
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            hr.q[ks] = __builtin_bit_cast(bf16x8, buf_load16(qr, 2u * ((16 * wave + l16) * kq_row + 32 * ks + 8 * g4)));
+            hr.q[ks] = __builtin_bit_cast(bf16x8, buf_load16(qr, 32 * ks + 8 * g4 < p.dkq
+                                                                     ? 2u * ((16 * wave + l16) * kq_row + 32 * ks + 8 * g4)
+                                                                     : kOff));
         // (the second k-step of P is all zero for rows below 32 and is then not used)
         const rsrc_t pr_ = make_rsrc(p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC) + kC * kC, 2u * (kC * kC));
 #pragma unroll
@@ -969,6 +974,7 @@ prefill_recurrent_kernel(PrefillParams p) {
     f32x4 H[MT];
     if (!helper) {
         const float* init = nullptr;
+        int init_rows = DK;                     // rows of the source tile (pool tiles have dkq)
         if (OUT) {
             // A split sequence starts its first segment from the state pass's
             // copy of the initial state (the source slot is then read only by
@@ -978,16 +984,21 @@ prefill_recurrent_kernel(PrefillParams p) {
             if (sg.split) {
                 init = (sg.k == 0 ? p.sh : p.se) + (static_cast<size_t>(sg.g0) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
             } else if (ssl >= 0) {
-                init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+                init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(p.dkq) * p.dv);
+                init_rows = p.dkq;
             }
         } else if (sg.first && ssl >= 0) {
-            init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv);
+            init = p.pool + (static_cast<size_t>(ssl) * p.hv + h) * (static_cast<size_t>(p.dkq) * p.dv);
+            init_rows = p.dkq;
         }
         if (init != nullptr) {
 #pragma unroll
             for (int mu = 0; mu < MT; ++mu)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) H[mu][i] = init[(16 * mu + 4 * g4 + i) * p.dv + col];
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * mu + 4 * g4 + i;
+                    H[mu][i] = row < init_rows ? init[row * p.dv + col] : 0.f;
+                }
         } else {
 #pragma unroll
             for (int mu = 0; mu < MT; ++mu)
@@ -1177,8 +1188,10 @@ prefill_recurrent_kernel(PrefillParams p) {
     // buffer resource: one lane offset and scalar row offsets (64-bit
     // per-element addresses would be hoisted out of the chunk loop and held in
     // registers for the whole pass)
-    auto store_tile = [&](float* tile) {
-        const rsrc_t cr = make_rsrc(tile, 4u * DK * p.dv);
+    // (rows past `rows` fall outside the range and are dropped: pool tiles
+    // have dkq rows, workspace tiles DK)
+    auto store_tile = [&](float* tile, int rows) {
+        const rsrc_t cr = make_rsrc(tile, 4u * rows * p.dv);
         const unsigned lo = 4u * (4 * g4 * p.dv + col);
 #pragma unroll
         for (int mu = 0; mu < MT; ++mu)
@@ -1196,7 +1209,7 @@ prefill_recurrent_kernel(PrefillParams p) {
             if (tid == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
             return;
         }
-        store_tile(p.pool + (static_cast<size_t>(ck) * p.hv + h) * (static_cast<size_t>(DK) * p.dv));
+        store_tile(p.pool + (static_cast<size_t>(ck) * p.hv + h) * (static_cast<size_t>(p.dkq) * p.dv), p.dkq);
     };
     if (OUT && sg.split) {
         // segments 2 and later: H <- M_j H + E_j for the transitions of the
@@ -1244,7 +1257,7 @@ prefill_recurrent_kernel(PrefillParams p) {
     }
     // the state pass keeps a copy of a split sequence's initial state for the
     // output pass's first segment
-    if (!OUT && sg.first) store_tile(p.sh + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv));
+    if (!OUT && sg.first) store_tile(p.sh + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv), DK);
     if (steps > 0) lds_barrier();
     for (int s = 0; s < steps; s += 2) {
         if (s < nch) {
@@ -1263,9 +1276,9 @@ prefill_recurrent_kernel(PrefillParams p) {
 
     if (OUT) {
         if (!sg.last) return;               // a middle segment's end state is the next one's start (pass 2)
-        store_tile(p.pool + (static_cast<size_t>(dsl) * p.hv + h) * (static_cast<size_t>(DK) * p.dv));
+        store_tile(p.pool + (static_cast<size_t>(dsl) * p.hv + h) * (static_cast<size_t>(p.dkq) * p.dv), p.dkq);
     } else if (!m_cols) {
-        store_tile(p.se + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv));
+        store_tile(p.se + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (static_cast<size_t>(DK) * p.dv), DK);
     } else {
         // transition M[d][m] (m = col), as bf16 high part and the bf16 rounding of the remainder
         uint16_t* out = p.sm + (static_cast<size_t>(blockIdx.y) * p.hv + h) * (2 * DK * DK);
@@ -1309,8 +1322,11 @@ int launch_dk(const PrefillParams& p, int nw, hipStream_t s) {
     const int groups = p.dv / (16 * nw);
     if (p.seg_len > 0) {
         // pass 1: every segment's local end state (value columns) and
-        // transition (dk identity columns), all segments at once
-        launch_recurrence<DK, kModeState>(p, nw, groups + DK / (16 * nw), s);
+        // transition (dk identity columns), all segments at once; its column
+        // groups are at most dk wide so that the transition columns split
+        // into whole groups
+        const int nws = gdn::prefill_state_waves(DK, p.dv);
+        launch_recurrence<DK, kModeState>(p, nws, p.dv / (16 * nws) + DK / (16 * nws), s);
         int st = check_launch("segment state pass");
         if (st != GDN_OK) return st;
     }
@@ -1356,6 +1372,7 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
     p.hk = a->num_k_heads;
     p.hv = a->num_v_heads;
     p.group = a->num_v_heads / a->num_k_heads;
+    p.dkq = a->dk;
     p.dv = a->dv;
     p.num_slots = pool->num_slots;
     p.scale = a->scale;
@@ -1382,8 +1399,8 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
         const int st = check_launch("chunk-offset");
         if (st != GDN_OK) return st;
     }
-    const int nw = a->dv >= 64 ? 4 : a->dv / 16;
-    switch (a->dk) {
+    const int nw = prefill_output_waves(a->dv);
+    switch (prefill_kernel_dk(a->dk)) {
         case 32: return launch_dk<32>(p, nw, s);
         case 64: return launch_dk<64>(p, nw, s);
         case 128: return launch_dk<128>(p, nw, s);

@@ -383,14 +383,23 @@ def test_prefill_f32_accepts_every_pool_shape_and_needs_only_offsets(lib):
         lib.gdn_state_pool_destroy(h)
 
 
-def test_prefill_unsupported_head_dim(lib):
-    buf, h = _make_pool(lib, hv=2, dk=16, dv=16)
+def test_prefill_dk16_runs_on_padded_dk32_tiles(lib):
+    """bf16 prefill at dk = 16 runs in the dk = 32 kernels (the MFMA k-step):
+    its workspace equals a dk = 32 call's, split sections included; other
+    chunk sizes stay unsupported."""
     _, addr = _fake_storage()
-    cuh = np.asarray([0, 8], np.int32)
-    a = _prefill_args(addr, cuh, dk=16, dv=16)
-    n = c_size_t()
-    assert lib.gdn_prefill_workspace_bytes(h, byref(a), byref(n)) == gdn.GDN_E_UNSUPPORTED
-    lib.gdn_state_pool_destroy(h)
+    cuh = np.asarray([0, 3000, 3090], np.int32)
+    sizes = []
+    for dk in (16, 32):
+        buf, h = _make_pool(lib, hv=2, dk=dk, dv=16)
+        a = _prefill_args(addr, cuh, dk=dk, dv=16)
+        n = c_size_t()
+        assert lib.gdn_prefill_workspace_bytes(h, byref(a), byref(n)) == gdn.GDN_OK
+        sizes.append(n.value)
+        a = _prefill_args(addr, cuh, dk=dk, dv=16, chunk_size=32)
+        assert lib.gdn_prefill_workspace_bytes(h, byref(a), byref(n)) == gdn.GDN_E_UNSUPPORTED
+        lib.gdn_state_pool_destroy(h)
+    assert sizes[0] == sizes[1]
 
 
 def _planned_segments(lib, cu, hv, dk, dv):
@@ -410,7 +419,8 @@ def _planned_segments(lib, cu, hv, dk, dv):
     N = len(cu) - 1
     chunks = int(np.sum((np.diff(np.asarray(cu, np.int64)) + 63) // 64))
     base = 2 * up(4 * (N + 1)) + up(2 * chunks * hv * 2 * 64 * 64) + up(4 * chunks * hv * 5 * 64)
-    per_seg = hv * (8 * dk * dv + 4 * dk * dk)
+    kdk = max(dk, 32)                    # dk = 16 runs on dk = 32 tiles
+    per_seg = hv * (8 * kdk * dv + 4 * kdk * kdk)
     extra = n.value - base
     assert extra >= 0 and extra % per_seg == 0
     return extra // per_seg
@@ -429,6 +439,6 @@ def test_planner_split_decisions(lib):
     # few heads leave the chip idle: a 3,000-token sequence is split, also at 64 value columns
     for dk, dv in ((128, 128), (64, 64), (128, 64)):
         assert _planned_segments(lib, [0, 3000, 3090], 4, dk, dv) > 2
-    # transitions work in 64-column groups: no split below 64
-    assert _planned_segments(lib, [0, 3000, 3090], 4, 32, 128) == 0
-    assert _planned_segments(lib, [0, 3000, 3090], 4, 128, 32) == 0
+    # small heads split too: the state pass's column groups are at most dk wide
+    for dk, dv in ((32, 128), (128, 32), (32, 32), (32, 16), (64, 16)):
+        assert _planned_segments(lib, [0, 3000, 3090], 4, dk, dv) > 2, (dk, dv)

@@ -92,7 +92,7 @@ def test_prefill_varlen_ragged_and_empty():
     np.testing.assert_array_equal(st.cpu().numpy()[:6], before[:6])
 
 
-@pytest.mark.parametrize("dk,dv", [(dk, dv) for dk in (32, 64, 128) for dv in (16, 32, 64, 128)])
+@pytest.mark.parametrize("dk,dv", [(dk, dv) for dk in (16, 32, 64, 128) for dv in (16, 32, 64, 128)])
 def test_prefill_head_shapes(dk, dv):
     lengths = [70, 129]
     src = [0, -1]
@@ -322,6 +322,25 @@ def test_split_dk_ne_dv():
                           num_slots=3, pool_sigma=0.05, src=src, g_range=(1e-3, 5e-2))
     o, st, _ = _gpu_prefill(pw, src, dst)
     _check(pw, o, st, src, dst)
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (32, 128), (128, 32), (32, 16), (64, 16), (128, 16), (32, 64), (16, 16),
+                                   (16, 128)])
+def test_split_small_heads(dk, dv):
+    """Split path below 64 columns: the state pass's column groups are at most
+    dk wide (dk = 32 with 64- or 128-column value groups in the output pass),
+    and 16- or 32-column value groups. A 3000-token sequence from a pool state
+    (split into several segments, so later segments start from states carried
+    through the transitions) beside a short one from zero, weak decay; a
+    second sequence in place."""
+    lengths = [3000, 90, 1200]
+    src = [0, -1, 3]
+    dst = [1, 2, 3]
+    pw = prefill_workload(f"split_small_{dk}x{dv}", seed=79 + dk + dv, lengths=lengths, HK=2, HV=4, dk=dk, dv=dv,
+                          dtype=BF16, num_slots=4, pool_sigma=0.05, src=src, g_range=(1e-3, 5e-2))
+    o, st, _ = _gpu_prefill(pw, src, dst)
+    _check(pw, o, st, src, dst)
+    np.testing.assert_array_equal(st.cpu().numpy()[0], pw.pool[0])
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64)])
