@@ -607,10 +607,28 @@ def bench_verify(reps=50, warmup=5):
     t = e0.elapsed_time(e1) / reps * 1e-3
     per_req = verify_bytes_per_request(K, wl.HK, wl.HV, wl.dk, wl.dv, 2)
     gbs = B * per_req / t / 1e9
+    # a copy of the same shape: the 64 source tiles (128 MiB) read once and
+    # written to K destinations each (torch's broadcast copy), back to back
+    tiles = storage[src.long()].contiguous()
+    out = torch.empty((K,) + tuple(tiles.shape), dtype=torch.float32, device="cuda")
+    copy = lambda: out.copy_(tiles.unsqueeze(0).expand_as(out))
+    copy()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        copy()
+    e1.record()
+    torch.cuda.synchronize()
+    tc = e0.elapsed_time(e1) / reps * 1e-3
+    copy_gbs = (1 + K) * tiles.numel() * 4 / tc / 1e9
+    del out, tiles
     pool.close()
     return {"workload": "spec_verify_bf16_b64_k4_hk16_hv32_128x128", "value": B * K / t, "unit": "draft tok/s",
             "us_per_launch": t * 1e6, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "bytes_per_launch": B * per_req,
+            "verify_shaped_copy_gbs": copy_gbs, "vs_verify_shaped_copy": gbs / copy_gbs,
+            "copy_protocol": f"the {B} source tiles x {wl.HV} heads read once and written to {K} destinations each "
+                             "(torch broadcast copy), back-to-back launches",
             "vs_decode_steps": "one launch reads each source tile once for 4 tokens; 4 decode steps would move "
                                f"{4 * B * decode_bytes_per_request(wl.HK, wl.HV, wl.dk, wl.dv, 2) / 1e6:.0f} MB "
                                f"against {B * per_req / 1e6:.0f} MB"}

@@ -116,26 +116,39 @@ struct DecodeShape {
     static_assert(NT % 64 == 0 && 64 % CG == 0 && DK % RG == 0, "unsupported tile shape");
 };
 
-// LDS scratch of one (request, head) workgroup.
+// LDS of one (request, head) workgroup: each wave's own copy of k^ and q~
+// (written and read by that wave alone), and the waves' partial reductions
+// in two sets, so that consecutive tokens of a verify chain alternate.
 template <int DK, int DV>
 struct TokenScratch {
-    float k[DK];
-    float q[DK];
-    f4 red[DecodeShape<DK, DV>::NW][DecodeShape<DK, DV>::CG][2];
+    float k[DecodeShape<DK, DV>::NW][DK];
+    float q[DecodeShape<DK, DV>::NW][DK];
+    f4 red[2][DecodeShape<DK, DV>::NW][DecodeShape<DK, DV>::CG][2];
 };
+
+// Orders a wave's own LDS writes before its later LDS reads (no other wave
+// takes part).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
 
 // One token of the rule on the tile slice this thread holds in registers (st):
 // normalise q and k (key head rows at qk_off), reduce H^T k^ and H^T q~ over
 // dk, write the token's output (row gh of o, v, g, beta) and leave the new tile
 // in st. When `out` (a (slot, head) tile) is given, each new row is also
 // stored as soon as it is formed, so the stores start while the rest of the
-// rows are still being read from LDS. `after_token` must be set when the
-// scratch was used by a previous token of the same workgroup (its last
-// readers are then waited for).
+// rows are still being read from LDS. Every wave normalises q and k itself
+// into its own LDS copy, so the only workgroup barrier of a token is the one
+// exchange of the waves' partial sums; `parity` alternates over a verify
+// chain's tokens, so one token's exchange never overwrites what the waves are
+// still reading of the previous one. (A wave's LDS operations complete in
+// order, so its k^ copy can be rewritten for the next token once read.)
 template <int DK, int DV, int DVW, typename T>
 __device__ __forceinline__ void token_update(const DecodeParams& p, size_t qk_off, size_t gh, int c0,
                                              f4 (&st)[DecodeShape<DK, DVW>::RPT], TokenScratch<DK, DVW>& sm,
-                                             bool after_token, f4* out) {
+                                             int parity, f4* out) {
     using Sh = DecodeShape<DK, DVW>;
     constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NW = Sh::NW;
     constexpr int KPL = (DK + 63) / 64;   // q/k elements per lane
@@ -145,8 +158,7 @@ __device__ __forceinline__ void token_update(const DecodeParams& p, size_t qk_of
     const int cg = tid % CG;
     const int rg = tid / CG;
 
-    // L2-normalise k and q (every wave computes the sums redundantly; wave 0
-    // publishes the normalised vectors)
+    // L2-normalise k and q in every wave, into the wave's own LDS copy
     float kx[KPL], qx[KPL];
     float sk = 0.f, sq = 0.f, skq = 0.f;
 #pragma unroll
@@ -170,18 +182,17 @@ __device__ __forceinline__ void token_update(const DecodeParams& p, size_t qk_of
     const float eg = expf(p.g[gh]);
     const float bt = p.beta[gh];
     const f4 vv = Elem<T>::load4(p.v, gh * DV + c0 + 4 * cg);
-    if (after_token) __syncthreads();        // the previous token's readers of sm.k are done
-    if (wave == 0) {
+    float* kw = sm.k[wave];
+    float* qw = sm.q[wave];
 #pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-            const int i = lane + 64 * e;
-            if (i < DK) {
-                sm.k[i] = kx[e] * rk;
-                sm.q[i] = qx[e] * rq;
-            }
+    for (int e = 0; e < KPL; ++e) {
+        const int i = lane + 64 * e;
+        if (i < DK) {
+            kw[i] = kx[e] * rk;
+            qw[i] = qx[e] * rq;
         }
     }
-    __syncthreads();
+    wave_lds_sync();
 
     // partial H^T k^ and H^T q~ over this thread's rows
     f4 a = f4{0.f, 0.f, 0.f, 0.f};
@@ -189,8 +200,8 @@ __device__ __forceinline__ void token_update(const DecodeParams& p, size_t qk_of
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int row = rg + RG * m;
-        a += st[m] * sm.k[row];
-        c += st[m] * sm.q[row];
+        a += st[m] * kw[row];
+        c += st[m] * qw[row];
     }
     // reduce over the row groups: lanes CG apart inside a wave, then the
     // waves through LDS, always in the same order (deterministic)
@@ -205,17 +216,20 @@ __device__ __forceinline__ void token_update(const DecodeParams& p, size_t qk_of
         c.z += __shfl_xor(c.z, off);
         c.w += __shfl_xor(c.w, off);
     }
-    if (lane < CG) {
-        sm.red[wave][lane][0] = a;
-        sm.red[wave][lane][1] = c;
-    }
-    __syncthreads();
-    f4 A = sm.red[0][cg][0];
-    f4 C = sm.red[0][cg][1];
+    f4 A = a, C = c;
+    if constexpr (NW > 1) {
+        if (lane < CG) {
+            sm.red[parity][wave][lane][0] = a;
+            sm.red[parity][wave][lane][1] = c;
+        }
+        __syncthreads();
+        A = sm.red[parity][0][cg][0];
+        C = sm.red[parity][0][cg][1];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-        A += sm.red[w][cg][0];
-        C += sm.red[w][cg][1];
+        for (int w = 1; w < NW; ++w) {
+            A += sm.red[parity][w][cg][0];
+            C += sm.red[parity][w][cg][1];
+        }
     }
 
     // delta correction, output, and the new tile
@@ -224,7 +238,7 @@ __device__ __forceinline__ void token_update(const DecodeParams& p, size_t qk_of
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int row = rg + RG * m;
-        st[m] = eg * st[m] + sm.k[row] * u;
+        st[m] = eg * st[m] + kw[row] * u;
         if (out != nullptr) __builtin_nontemporal_store(st[m], out + row * (DV / 4) + c0 / 4 + cg);
     }
 }
@@ -275,15 +289,20 @@ __global__ void __launch_bounds__(decode_threads(DK, DVW)) gdn_decode_kernel(Dec
     f4 st[DecodeShape<DK, DVW>::RPT];
     load_tile<DK, DV, DVW>(p, s, h, c0, st);
     const size_t qk_off = (static_cast<size_t>(b) * p.hk + h / p.group) * DK;
-    token_update<DK, DV, DVW, T>(p, qk_off, static_cast<size_t>(b) * p.hv + h, c0, st, sm, false,
+    token_update<DK, DV, DVW, T>(p, qk_off, static_cast<size_t>(b) * p.hv + h, c0, st, sm, 0,
                                  tile_ptr(p, d, h, DK * DV));
 }
 
 // Speculative-decode verification: draft tokens 0 .. n-1 of request b in
 // order on the slice held in registers; the slice goes to dst[b][i] after
 // token i when that entry is >= 0. The source is read once for all of them.
+// Every token ends in a slice store, so residency hides more latency than
+// registers save: the kernel is held to at most 128 VGPRs (four waves per
+// SIMD), which measured faster than the uncapped build even where the
+// 128-wide slice then spills a few registers.
 template <int DK, int DV, int DVW, typename T>
-__global__ void __launch_bounds__(decode_threads(DK, DVW)) gdn_verify_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(decode_threads(DK, DVW)) __attribute__((amdgpu_waves_per_eu(4, 8)))
+gdn_verify_kernel(DecodeParams p) {
     constexpr int NS = DV / DVW;
     __shared__ TokenScratch<DK, DVW> sm;
     const unsigned tile = blockIdx.x / NS;
@@ -310,7 +329,7 @@ __global__ void __launch_bounds__(decode_threads(DK, DVW)) gdn_verify_kernel(Dec
     for (int i = 0; i < n; ++i) {
         const size_t t = static_cast<size_t>(b) * K + i;      // token row
         const int d = p.dst[t];
-        token_update<DK, DV, DVW, T>(p, (t * p.hk + j) * DK, t * p.hv + h, c0, st, sm, i > 0,
+        token_update<DK, DV, DVW, T>(p, (t * p.hk + j) * DK, t * p.hv + h, c0, st, sm, i & 1,
                                      d >= 0 ? tile_ptr(p, d, h, DK * DV) : nullptr);
     }
 }
