@@ -44,7 +44,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
-FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 MFMA, TFLOP/s
 METRIC = "GDN decode state-update HBM GB/s (% peak); chunked prefill tokens/s (MFMA %)"
 
 
@@ -531,14 +531,19 @@ def bench_prefill_long_context(tokens=1 << 20, reps=3):
 
 
 def bench_prefill_f32(reps=5):
-    """Prefill with float32 inputs (the fp32 token recurrence) at 16/32 heads,
-    128 x 128: one 8192-token sequence, and 16 sequences of 800 tokens from
-    zero states. Flops: 6 dk dv per token and value head (H^T k, H^T q and
-    the rank-one update), against the fp32 vector peak."""
+    """Prefill with float32 inputs at 16/32 heads, 128 x 128: one 8192-token
+    sequence, and 16 sequences of 800 tokens from zero states. The chunk form
+    runs with every product on the fp32 MFMA. Flops are the chunk form's
+    algorithmic count per token and value head: 6 dk dv (K H, Q H and the
+    state advance), 2 (C + 1) dv (the triangular T R and P U), 2 C dk / G (the
+    triangular Gram matrices, shared by the G value heads of a key head) and
+    C^2 / 3 (the triangular solve), C = 64; against the dense fp32 MFMA peak."""
     import torch
     from hybrid_linear_attention_02_amd import gdn
     from hybrid_linear_attention_02_amd.workloads import F32, prefill_workload
 
+    C, G, dk, dv = 64, 2, 128, 128
+    flops_per_tok = 6 * dk * dv + 2 * (C + 1) * dv + 2 * C * dk / G + C * C / 3
     out = {}
     for name, lengths in (("one_seq_t8192", [8192]), ("packed_16x800", [800] * 16)):
         pw = prefill_workload(name, seed=2, lengths=lengths, HK=16, HV=32, dk=128, dv=128, dtype=F32,
@@ -563,12 +568,12 @@ def bench_prefill_f32(reps=5):
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / reps * 1e-3
         T = int(pw.cu_seqlens[-1])
-        tflops = 6 * 128 * 128 * 32 * T / t / 1e12
+        tflops = flops_per_tok * 32 * T / t / 1e12
         out[name] = {"ms": round(t * 1e3, 3), "tok_per_s": round(T / t, 1),
-                     "us_per_token_step": round(t * 1e6 / max(lengths), 3),
-                     "tflops_fp32": round(tflops, 2), "frac_fp32_valu": round(tflops / FP32_VALU_PEAK_TFLOPS, 4)}
+                     "tflops_fp32": round(tflops, 2), "frac_fp32_mfma": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4)}
         pool.close()
-    out["bound"] = "alu (a latency-bound chain per token; the state stays in registers)"
+    out["bound"] = "mfma (fp32 16x16x4; the chunk recurrence is sequential per (sequence, head, 16 columns))"
+    out["flops_per_token_head"] = flops_per_tok
     return out
 
 

@@ -32,7 +32,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 # Per-source extra flags. The prefill kernels keep their MFMA accumulators in
 # ordinary VGPRs (the unified register file of gfx950), which saves the
 # accumulator-register copies around every post-processed MFMA result.
-EXTRA = {"gdn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"gdn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gdn_prefill_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -192,7 +192,7 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     int st = check_heads(pool, a->num_k_heads, a->num_v_heads, a->dk, a->dv, fn);
     if (st != GDN_OK) return st;
     if (a->chunk_size != 64) return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: chunk_size must be 64");
-    const bool f32 = a->dtype == GDN_DTYPE_F32;   // token recurrence, any pool head shape
+    const bool f32 = a->dtype == GDN_DTYPE_F32;   // chunked form on the fp32 MFMA, any pool head shape
     if (a->dtype != GDN_DTYPE_BF16 && !f32)
         return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: dtype must be GDN_DTYPE_BF16 or GDN_DTYPE_F32");
     if (!f32 && !prefill_dims_supported(a->dk, a->dv))
@@ -239,9 +239,11 @@ int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* p
     plan->off_seg_offsets = off;
     off = up(off + sizeof(int32_t) * static_cast<size_t>(n + 1));
     plan->off_tp = off;
-    off = up(off + (f32 ? 0 : 2ull * chunks * hv * 2 * 64 * 64));
+    // T and P per (chunk, value head): bf16 64 x 64 each, or fp32 as the ten
+    // lower 16 x 16 blocks each
+    off = up(off + (f32 ? 4ull * chunks * hv * 2 * (10 * 64 * 4) : 2ull * chunks * hv * 2 * 64 * 64));
     plan->off_sc = off;
-    off = up(off + (f32 ? 0 : 4ull * chunks * hv * (5 * 64)));
+    off = up(off + 4ull * chunks * hv * (5 * 64));
     plan->off_se = off;
     off = up(off + (split ? 4ull * segs * hv * dk * dv : 0));
     plan->off_sm = off;
@@ -279,6 +281,5 @@ extern "C" int gdn_prefill_chunked(const gdn_pool* pool, const gdn_prefill_args*
     if (workspace_bytes < plan.bytes)
         return fail(GDN_E_INVALID, "gdn_prefill_chunked: workspace too small (need " + std::to_string(plan.bytes) +
                                        " bytes)");
-    if (a->dtype == GDN_DTYPE_F32) return gdn::launch_prefill_f32(pool, a, plan, workspace, stream);
     return gdn::launch_prefill(pool, a, plan, workspace, stream);
 }

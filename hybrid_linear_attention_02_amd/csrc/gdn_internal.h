@@ -65,7 +65,8 @@ struct PrefillPlan {
     int32_t num_segs = 0;         // total segments
     size_t off_chunk_offsets = 0; // int32 [N+1]: first chunk of each sequence
     size_t off_seg_offsets = 0;   // int32 [N+1]: first segment of each sequence
-    size_t off_tp = 0;            // bf16 [chunks][HV][2][64 * 64]: T and P as row-operand fragments
+    size_t off_tp = 0;            // T and P: bf16 [chunks][HV][2][64 * 64] row-operand fragments, or for
+                                  // float32 inputs fp32 [chunks][HV][2][10][64][4] block fragments
     size_t off_sc = 0;            // float [chunks][HV][5][64]: per-token scale rows
     size_t off_se = 0;            // float [segs][HV][dk][dv]: local end state E (split only)
     size_t off_sm = 0;            // bf16 [segs][HV][2][dk][dk]: transition M, high then low part (split only)
@@ -73,10 +74,9 @@ struct PrefillPlan {
     size_t bytes = 0;
 };
 int plan_prefill(const gdn_pool* pool, const gdn_prefill_args* a, PrefillPlan* plan);
+// bf16 inputs: chunked form on the bf16 MFMA; float32 inputs: chunked form
+// on the fp32 MFMA
 int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const PrefillPlan& plan,
                    void* workspace, void* stream);
-// float32 inputs: the per-token rule in fp32 (chunk offsets in the workspace)
-int launch_prefill_f32(const gdn_pool* pool, const gdn_prefill_args* a, const PrefillPlan& plan,
-                       void* workspace, void* stream);
 
 }  // namespace gdn

@@ -45,106 +45,11 @@
 #include <string>
 
 #include "gdn_internal.h"
+#include "gdn_prefill_common.h"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-constexpr int kC = 64;        // chunk length
-constexpr int kScRows = 5;    // per-token scale rows in the workspace
-
-// Rows of the per-(chunk, head) scale block.
-enum : int {
-    kScX = 0,     // exp(gamma_r) rk_r            scales X = K H
-    kScBeta = 1,  // beta_r
-    kScZ = 2,     // exp(gamma_r) rq_r            scales Z = Q H
-    kScD = 3,     // rk_r exp(gamma_last - gamma_r)  scales U in the state advance
-    kScE = 4,     // exp(gamma_last)              (every entry)
-};
-
-constexpr int kInlineSeqs = 32;
-
-struct PrefillParams {
-    const int32_t* cu;          // [N+1] device
-    const int32_t* chunk_off;   // [N+1] device (workspace): first chunk of each sequence
-    const uint16_t* q;          // [T][HK][DK] bf16 bits
-    const uint16_t* k;
-    const uint16_t* v;          // [T][HV][DV]
-    const float* g;             // [T][HV]
-    const float* beta;
-    uint16_t* o;                // [T][HV][DV]
-    float* pool;
-    const int32_t* src;
-    const int32_t* dst;
-    int32_t* err;
-    const int32_t* ckpt;        // [chunks] device or null: slot receiving the state after each chunk
-    uint16_t* tp;               // [chunks][HV][2][64 * 64] T, then P, as row-operand fragments
-    float* sc;                  // [chunks][HV][5][64]    scale rows
-    int32_t* chunk_off_w;       // same buffer as chunk_off, written by the prep kernel
-    const int32_t* seg_off;     // [N+1] device (workspace): first segment of each sequence
-    int32_t* seg_off_w;
-    float* se;                  // [segs][HV][DK][DV]   local end state E of each segment (split only)
-    uint16_t* sm;               // [segs][HV][2][DK][DK] transition M, bf16 high and low parts (split only)
-    float* sh;                  // [segs][HV][DK][DV]   copy of the initial state at a split sequence's first segment
-    int32_t seg_len;            // chunks per segment; 0 = one segment per sequence
-    int32_t num_segs;
-    int32_t n_seqs;
-    int32_t num_chunks;
-    int32_t total_tokens;
-    int32_t hk;
-    int32_t hv;
-    int32_t group;
-    int32_t dkq;                // dk of q, k and the pool tiles; the kernels run at DK >= dkq
-                                // (dk = 16 runs at DK = 32 with zero-padded rows and columns)
-    int32_t dv;
-    int32_t num_slots;
-    float scale;
-    float eps;
-    // For calls of at most kInlineSeqs sequences the host fills both offset
-    // tables here (the kernel arguments) and the prep kernel is not launched;
-    // inl_n is then n_seqs, else 0.
-    int32_t inl_n;
-    int32_t inl_chunk[kInlineSeqs + 1];
-    int32_t inl_seg[kInlineSeqs + 1];
-};
-
-// Chunk range [c0, c1) and segment range [s0, s1) of sequence n.
-struct SeqSpan {
-    int n, c0, c1, s0, s1;
-};
-
-// The span of the sequence holding chunk `key` (BY_SEG false) or segment
-// `key` (BY_SEG true): the last sequence whose first chunk (segment) is
-// <= key. `key` is wave-uniform. The kernel-argument tables are only ever
-// indexed by constants (a fully unrolled scan), so they stay in the argument
-// segment instead of being copied to private memory.
-template <bool BY_SEG>
-__device__ __forceinline__ SeqSpan find_span(const PrefillParams& p, int key) {
-    SeqSpan r;
-    if (p.inl_n > 0) {
-        r = SeqSpan{0, p.inl_chunk[0], p.inl_chunk[1], p.inl_seg[0], p.inl_seg[1]};
-        if (p.inl_n == 1) return r;
-#pragma unroll
-        for (int i = 1; i < kInlineSeqs; ++i) {
-            if (i < p.inl_n && (BY_SEG ? p.inl_seg[i] : p.inl_chunk[i]) <= key)
-                r = SeqSpan{i, p.inl_chunk[i], p.inl_chunk[i + 1], p.inl_seg[i], p.inl_seg[i + 1]};
-        }
-        return r;
-    }
-    const int32_t* off = BY_SEG ? p.seg_off : p.chunk_off;
-    int lo = 0, hi = p.n_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= key) lo = mid;
-        else hi = mid - 1;
-    }
-    return SeqSpan{lo, p.chunk_off[lo], p.chunk_off[lo + 1], p.seg_off[lo], p.seg_off[lo + 1]};
-}
+using namespace gdn::pf;
 
 // Uniform base pointer plus a 32-bit per-lane byte offset: lets the compiler
 // use the scalar-base global access form (no 64-bit address per lane).
@@ -158,21 +63,6 @@ __device__ __forceinline__ const T* at_bytes(const B* base, unsigned byte_off) {
     return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
 }
 
-// Buffer resources (base, byte range): loads past the range return zero and
-// stores past it are dropped, in hardware, so ragged rows need no branch.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, unsigned off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, unsigned off) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-__device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, unsigned off) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, 0, 0);
-}
 // Byte range of `rows` token rows of `width` bf16 values, rows `stride`
 // elements apart (zero rows: an empty range).
 __device__ __forceinline__ unsigned rows_bytes(int rows, unsigned stride, int width) {
@@ -196,10 +86,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-// 2^x on the hardware exp2 (v_exp_f32). Arguments here are <= 0 decay
-// exponents; results below the normal range flush to zero, which is the
-// decay factor's limit anyway.
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 8 bf16 from two fp32 accumulator quads: slots 0-3 <- a, 4-7 <- b.
 __device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b) {
@@ -312,16 +198,6 @@ __device__ __forceinline__ bf16x8 kq_tr_pair(const uint16_t* buf, int row0, int 
     return as_bf16x8(w);
 }
 
-// Workgroup barrier that orders LDS only. A plain __syncthreads() also waits
-// for every outstanding global load and store of the wave (the workgroup
-// release fence covers global memory), which would put a full memory round
-// trip on every chunk; the kernels here exchange data between waves through
-// LDS alone.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // ---------------------------------------------------------------------------
 // prep: first chunk and first segment of every sequence
@@ -390,20 +266,14 @@ __global__ void __launch_bounds__(kOffThreads) chunk_offsets_kernel(PrefillParam
 // key head's group
 // ---------------------------------------------------------------------------
 
-// fp32 16 x 16 x 16 product on the fp32 MFMA: acc += X Y, with X given with
-// one row per lane (lane (row, g) holds X[row][4 g + e]) and Y in accumulator
-// layout (lane (column, g) holds Y[4 g + e][column]). Step kk contracts
-// k = 4 g + kk, so both operands are read in place. Swapping the arguments
-// yields (X Y)^T in accumulator layout, i.e. X Y with one row per lane.
-__device__ __forceinline__ f32x4 mm16(f32x4 x, f32x4 y, f32x4 acc) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[kk], y[kk], acc, 0, 0, 0);
-    return acc;
-}
-
-template <int DK>
+// F32: float32 q and k (any dk that is a multiple of 16), Gram matrices on the
+// fp32 MFMA, T and P written as fp32 row fragments (p.tpf); otherwise bf16
+// q and k, Gram matrices on the bf16 MFMA, T and P as bf16 row-operand
+// fragments (p.tp). The decay, A, the solve for T and the scale rows are the
+// same fp32 arithmetic in both.
+template <int DK, bool F32>
 __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
-    constexpr int KS = DK / 32;       // MFMA k-steps over dk
+    constexpr int KS = F32 ? 1 : DK / 32;   // bf16 MFMA k-steps over dk
     // The four 16 x 16 diagonal blocks of a 64 x 64 matrix in LDS: block b
     // at b * BS floats, rows of 16 floats. The 16-float gap between blocks
     // puts the four lane groups (one per block) on different banks.
@@ -428,38 +298,6 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
     const int len = min(kC, tend - t0);
     if (len <= 0 || tend > p.total_tokens || p.dst[n] < 0) return;
 
-    // raw k and q rows as row operands in natural feature order (a
-    // contraction over dk may order its k slots freely, as long as both
-    // operands agree): kr[tt][ks] = K[16 tt + l16][32 ks + 8 g .. +7]. All
-    // of them are requested before any is used, so the wave waits for one
-    // global round trip, not five.
-    const auto load_rows = [&](const uint16_t* x, int tt, u32x4* dst) {
-        const int r = 16 * tt + l16;
-        const size_t base = (static_cast<size_t>(t0 + r) * p.hk + j) * p.dkq + 8 * g4;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            dst[ks] = (r < len && 32 * ks + 8 * g4 < p.dkq) ? *reinterpret_cast<const u32x4*>(x + base + 32 * ks)
-                                                             : u32x4{0u, 0u, 0u, 0u};
-    };
-    // sum of squares of the row held in operand layout, over all four lane groups
-    const auto row_sumsq = [&](const u32x4* xr) {
-        float acc = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float x0 = __uint_as_float(xr[ks][e] << 16), x1 = __uint_as_float(xr[ks][e] & 0xffff0000u);
-                acc += x0 * x0 + x1 * x1;
-            }
-        acc += __shfl_xor(acc, 16);
-        acc += __shfl_xor(acc, 32);
-        return acc;
-    };
-    u32x4 kr[4][KS], qa[4][KS];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) load_rows(p.k, tt, kr[tt]);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) load_rows(p.q, tt, qa[tt]);
     // per-token g, beta of value head h (token = lane)
     const auto load_gb = [&](int h, float& gl, float& bl) {
         gl = 0.f;
@@ -471,41 +309,128 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         }
     };
     float gl_next, bl_next;
-    load_gb(j * p.group, gl_next, bl_next);
-
     // Shared by the group's value heads: the L2 norms of the k and q rows
-    // (fp32 sums of exact bf16 squares) and the raw Gram tiles on MFMA with
-    // one row per lane (each product takes the column tile's k rows as its
-    // first operand): gkk[tr][ts] = K_ts K_tr^T, gkq = K_ts Q_tr^T, ts <= tr,
-    // packed as index tr (tr + 1) / 2 + ts.
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const float sk = row_sumsq(kr[tt]);
-        const int r = 16 * tt + l16;
-        if (g4 == 0) sRk[r] = (r < len) ? __builtin_amdgcn_rsqf(sk + p.eps) : 0.f;
-    }
+    // (row scales rk in sRk, rq = scale / |q| in rqv and sRq) and the raw Gram
+    // tiles with one row per lane (each product takes the column tile's k
+    // rows as its first operand): gkk[tr][ts] = K_ts K_tr^T, gkq = K_ts Q_tr^T,
+    // ts <= tr, packed as index tr (tr + 1) / 2 + ts.
     float rqv[4];
-#pragma unroll
-    for (int tr = 0; tr < 4; ++tr) {
-        const int r = 16 * tr + l16;
-        rqv[tr] = (r < len) ? p.scale * __builtin_amdgcn_rsqf(row_sumsq(qa[tr]) + p.eps) : 0.f;
-        if (g4 == 0) sRq[r] = rqv[tr];
-    }
     f32x4 gkk[10], gkq[10];
+    if constexpr (F32) {
+        load_gb(j * p.group, gl_next, bl_next);
+        // fp32 rows in blocks of 16 features, lane (row, g) holding
+        // X[row][16 b + 4 g + e]; sums of squares and the Gram tiles
+        // accumulate block by block (one block of k and q rows in flight)
+        float sk[4] = {0.f, 0.f, 0.f, 0.f}, sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tr = 0; tr < 4; ++tr)
-#pragma unroll
-        for (int ts = 0; ts <= tr; ++ts) {
-            f32x4 kk = f32x4{0.f, 0.f, 0.f, 0.f}, kq = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 bk = as_bf16x8(kr[ts][ks]);
-                kk = mfma16(bk, as_bf16x8(kr[tr][ks]), kk);
-                kq = mfma16(bk, as_bf16x8(qa[tr][ks]), kq);
-            }
-            gkk[tr * (tr + 1) / 2 + ts] = kk;
-            gkq[tr * (tr + 1) / 2 + ts] = kq;
+        for (int i = 0; i < 10; ++i) {
+            gkk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            gkq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
+        for (int b = 0; b < DK / 16; ++b) {
+            f32x4 kb[4], qb[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int r = 16 * tt + l16;
+                const size_t off = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + 16 * b + 4 * g4;
+                kb[tt] = r < len ? *reinterpret_cast<const f32x4*>(p.kf + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+                qb[tt] = r < len ? *reinterpret_cast<const f32x4*>(p.qf + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sk[tt] += kb[tt][e] * kb[tt][e];
+                    sq[tt] += qb[tt][e] * qb[tt][e];
+                }
+#pragma unroll
+            for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+                for (int ts = 0; ts <= tr; ++ts) {
+                    const int ix = tr * (tr + 1) / 2 + ts;
+                    gkk[ix] = mm16(kb[ts], kb[tr], gkk[ix]);
+                    gkq[ix] = mm16(kb[ts], qb[tr], gkq[ix]);
+                }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            float a = sk[tt], b = sq[tt];
+            a += __shfl_xor(a, 16);
+            a += __shfl_xor(a, 32);
+            b += __shfl_xor(b, 16);
+            b += __shfl_xor(b, 32);
+            const int r = 16 * tt + l16;
+            rqv[tt] = (r < len) ? p.scale * __builtin_amdgcn_rsqf(b + p.eps) : 0.f;
+            if (g4 == 0) {
+                sRk[r] = (r < len) ? __builtin_amdgcn_rsqf(a + p.eps) : 0.f;
+                sRq[r] = rqv[tt];
+            }
+        }
+    } else {
+        // raw k and q rows as row operands in natural feature order (a
+        // contraction over dk may order its k slots freely, as long as both
+        // operands agree): kr[tt][ks] = K[16 tt + l16][32 ks + 8 g .. +7]. All
+        // of them are requested before any is used, so the wave waits for one
+        // global round trip, not five.
+        const auto load_rows = [&](const uint16_t* x, int tt, u32x4* dst) {
+            const int r = 16 * tt + l16;
+            const size_t base = (static_cast<size_t>(t0 + r) * p.hk + j) * p.dkq + 8 * g4;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                dst[ks] = (r < len && 32 * ks + 8 * g4 < p.dkq) ? *reinterpret_cast<const u32x4*>(x + base + 32 * ks)
+                                                                 : u32x4{0u, 0u, 0u, 0u};
+        };
+        // sum of squares of the row held in operand layout, over all four lane groups
+        const auto row_sumsq = [&](const u32x4* xr) {
+            float acc = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = __uint_as_float(xr[ks][e] << 16), x1 = __uint_as_float(xr[ks][e] & 0xffff0000u);
+                    acc += x0 * x0 + x1 * x1;
+                }
+            acc += __shfl_xor(acc, 16);
+            acc += __shfl_xor(acc, 32);
+            return acc;
+        };
+        u32x4 kr[4][KS], qa[4][KS];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) load_rows(p.k, tt, kr[tt]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) load_rows(p.q, tt, qa[tt]);
+        load_gb(j * p.group, gl_next, bl_next);
+
+        // norms from fp32 sums of the exact bf16 squares, Gram tiles on the
+        // bf16 MFMA
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const float sk = row_sumsq(kr[tt]);
+            const int r = 16 * tt + l16;
+            if (g4 == 0) sRk[r] = (r < len) ? __builtin_amdgcn_rsqf(sk + p.eps) : 0.f;
+        }
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr) {
+            const int r = 16 * tr + l16;
+            rqv[tr] = (r < len) ? p.scale * __builtin_amdgcn_rsqf(row_sumsq(qa[tr]) + p.eps) : 0.f;
+            if (g4 == 0) sRq[r] = rqv[tr];
+        }
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+            for (int ts = 0; ts <= tr; ++ts) {
+                f32x4 kk = f32x4{0.f, 0.f, 0.f, 0.f}, kq = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 bk = as_bf16x8(kr[ts][ks]);
+                    kk = mfma16(bk, as_bf16x8(kr[tr][ks]), kk);
+                    kq = mfma16(bk, as_bf16x8(qa[tr][ks]), kq);
+                }
+                gkk[tr * (tr + 1) / 2 + ts] = kk;
+                gkq[tr * (tr + 1) / 2 + ts] = kq;
+            }
+    }
 
     for (int hig = 0; hig < p.group; ++hig) {
         const int h = j * p.group + hig;
@@ -527,7 +452,9 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
 
         // A (strictly lower), kept in registers off the diagonal and in LDS
         // on it, and P, which goes to the workspace as row-operand fragments
-        u32x4* Pf = reinterpret_cast<u32x4*>(p.tp + ((static_cast<size_t>(c) * p.hv + h) * 2 + 1) * (kC * kC));
+        const size_t mat = (static_cast<size_t>(c) * p.hv + h) * 2;     // T of this (chunk, head); P follows
+        u32x4* Pf = F32 ? nullptr : reinterpret_cast<u32x4*>(p.tp + (mat + 1) * (kC * kC));
+        f32x4* Pf32 = F32 ? reinterpret_cast<f32x4*>(p.tpf + (mat + 1) * kFragFloats) : nullptr;
         f32x4 ra[6];                           // A blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr) {
@@ -557,9 +484,15 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
                 if (ts == tr) *reinterpret_cast<f32x4*>(sAT + tr * BS + l16 * SD + 4 * g4) = a;
                 else ra[tr * (tr - 1) / 2 + ts] = a;
             }
+            if constexpr (F32) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)   // (rows below 32 have an all-zero second k-step: not written)
-                if (ks == 0 || tr >= 2) Pf[(tr * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(pt[2 * ks], pt[2 * ks + 1]));
+                for (int ts = 0; ts <= tr; ++ts) Pf32[(tr * (tr + 1) / 2 + ts) * 64 + lane] = pt[ts];
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)   // (rows below 32 have an all-zero second k-step: not written)
+                    if (ks == 0 || tr >= 2)
+                        Pf[(tr * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(pt[2 * ks], pt[2 * ks + 1]));
+            }
         }
         lds_barrier();
         {
@@ -624,19 +557,35 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         S = mm16(ra[5], t20c, mm16(ra[4], t10c, mm16(ra[3], tc[0], z)));   // A30 T00 + A31 T10 + A32 T20
         const f32x4 t30r = -mm16(S, trf[3], z);
 
-        // T to the workspace as row-operand fragments (tau, ks) = rows 16 tau ..,
-        // k block 32 ks: blocks (tau, 2 ks) and (tau, 2 ks + 1); the two all-zero
-        // fragments (0, 1) and (1, 1) are not written
-        u32x4* Tf = reinterpret_cast<u32x4*>(p.tp + (static_cast<size_t>(c) * p.hv + h) * 2 * (kC * kC));
-        auto put = [&](int tau, int ks, f32x4 lo, f32x4 hi) {
-            Tf[(tau * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(lo, hi));
-        };
-        put(0, 0, trf[0], z);
-        put(1, 0, t10r, trf[1]);
-        put(2, 0, t20r, t21r);
-        put(2, 1, trf[2], z);
-        put(3, 0, t30r, t31r);
-        put(3, 1, t32r, trf[3]);
+        if constexpr (F32) {
+            // T to the workspace as fp32 row fragments of its ten lower blocks
+            f32x4* Tf = reinterpret_cast<f32x4*>(p.tpf + mat * kFragFloats);
+            auto put = [&](int tau, int jb, f32x4 x) { Tf[(tau * (tau + 1) / 2 + jb) * 64 + lane] = x; };
+            put(0, 0, trf[0]);
+            put(1, 0, t10r);
+            put(1, 1, trf[1]);
+            put(2, 0, t20r);
+            put(2, 1, t21r);
+            put(2, 2, trf[2]);
+            put(3, 0, t30r);
+            put(3, 1, t31r);
+            put(3, 2, t32r);
+            put(3, 3, trf[3]);
+        } else {
+            // T to the workspace as row-operand fragments (tau, ks) = rows 16 tau ..,
+            // k block 32 ks: blocks (tau, 2 ks) and (tau, 2 ks + 1); the two all-zero
+            // fragments (0, 1) and (1, 1) are not written
+            u32x4* Tf = reinterpret_cast<u32x4*>(p.tp + mat * (kC * kC));
+            auto put = [&](int tau, int ks, f32x4 lo, f32x4 hi) {
+                Tf[(tau * 2 + ks) * 64 + lane] = __builtin_bit_cast(u32x4, pack8(lo, hi));
+            };
+            put(0, 0, trf[0], z);
+            put(1, 0, t10r, trf[1]);
+            put(2, 0, t20r, t21r);
+            put(2, 1, trf[2], z);
+            put(3, 0, t30r, t31r);
+            put(3, 1, t32r, trf[3]);
+        }
     }
 }
 
@@ -1312,10 +1261,22 @@ void launch_recurrence(const PrefillParams& p, int nw, int groups, hipStream_t s
     }
 }
 
+// float32 inputs: the intra-chunk kernel in its fp32 form, then the fp32
+// recurrence (no sequence split)
+template <int DK>
+int launch_dk_f32(const PrefillParams& p, hipStream_t s) {
+    if (p.num_chunks > 0) {
+        hipLaunchKernelGGL((prefill_intra_kernel<DK, true>), dim3(p.num_chunks, p.hk), dim3(64), 0, s, p);
+        const int st = check_launch("fp32 intra-chunk");
+        if (st != GDN_OK) return st;
+    }
+    return launch_f32_recurrence(p, s);
+}
+
 template <int DK>
 int launch_dk(const PrefillParams& p, int nw, hipStream_t s) {
     if (p.num_chunks > 0) {
-        hipLaunchKernelGGL((prefill_intra_kernel<DK>), dim3(p.num_chunks, p.hk), dim3(64), 0, s, p);
+        hipLaunchKernelGGL((prefill_intra_kernel<DK, false>), dim3(p.num_chunks, p.hk), dim3(64), 0, s, p);
         const int st = check_launch("intra-chunk");
         if (st != GDN_OK) return st;
     }
@@ -1352,6 +1313,11 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
     p.g = a->g;
     p.beta = a->beta;
     p.o = static_cast<uint16_t*>(a->o);
+    p.qf = static_cast<const float*>(a->q);
+    p.kf = static_cast<const float*>(a->k);
+    p.vf = static_cast<const float*>(a->v);
+    p.of = static_cast<float*>(a->o);
+    p.tpf = reinterpret_cast<float*>(ws + plan.off_tp);
     p.pool = pool->storage;
     p.src = a->src_slots;
     p.dst = a->dst_slots;
@@ -1398,6 +1364,15 @@ int launch_prefill(const gdn_pool* pool, const gdn_prefill_args* a, const Prefil
         hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(kOffThreads), 0, s, p);
         const int st = check_launch("chunk-offset");
         if (st != GDN_OK) return st;
+    }
+    if (a->dtype == GDN_DTYPE_F32) {
+        switch (a->dk) {
+            case 16: return launch_dk_f32<16>(p, s);
+            case 32: return launch_dk_f32<32>(p, s);
+            case 64: return launch_dk_f32<64>(p, s);
+            case 128: return launch_dk_f32<128>(p, s);
+            default: return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: unsupported dk");
+        }
     }
     const int nw = prefill_output_waves(a->dv);
     switch (prefill_kernel_dk(a->dk)) {

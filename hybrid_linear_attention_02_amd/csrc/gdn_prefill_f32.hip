@@ -1,24 +1,37 @@
-// Prefill of float32 inputs: the gated delta rule token by token in fp32.
+// Prefill of float32 inputs: the chunked gated delta rule on the fp32 MFMA
+// (v_mfma_f32_16x16x4_f32), for results within fp32 rounding of the token
+// recurrence.
 //
-// The chunked form of the bf16 prefill feeds its products to bf16 matrix
-// cores; with float32 inputs that rounding would dominate the error, so
-// float32 sequences run the per-token rule directly (the same arithmetic as
-// decode), with the state held in registers for the whole sequence:
+// The chunk form is the one of the bf16 prefill (the WY / UT form of the
+// delta rule over chunks of C = 64 tokens):
 //
-//   a = H^T k^,  c = H^T q~,  u = beta (v - exp(g) a),
-//   o = exp(g) c + u (k^ . q~),  H' = exp(g) H + k^ u^T.
+//   U  = T diag(beta) (V - diag(exp(gamma) rk) K H)
+//   O  = diag(exp(gamma) rq) Q H + P U
+//   H' = exp(gamma_last) H + K^T diag(rk exp(gamma_last - gamma)) U
 //
-// One wavefront per (sequence, value head, column slice of 4, 8 or 16
-// columns): the columns of H are independent under the rule, so the slices
-// are too, and thin slices let a single long sequence occupy the chip. Each
-// lane holds a few consecutive rows of its slice and loads those rows of k
-// and q itself, so the per-token work needs no LDS and no barrier: the sums
-// over dk are DPP and lane-swap reductions inside the wavefront. The next
-// token's inputs are loaded while the current one runs. The slice goes to
-// the checkpoint slots at the chosen 64-token chunk ends and to the
-// destination at the end; source slots are only read (copy-on-write, as in
-// the TokenSpeed article, 24-ai.news, English, section "What are the key
-// optimizations behind the record?").
+// with raw q and k rows, their L2 norms applied as the row scales rk and rq
+// (rq includes the attention scale). The intra-chunk kernel of the bf16
+// prefill, instantiated for float32 rows, computes T = (I + A)^-1, P and the
+// per-token scale rows of every (chunk, value head) into the workspace, with
+// every product on the fp32 MFMA. This file holds the recurrence across
+// chunks.
+//
+// Recurrence: one workgroup of four waves per (sequence, value head, 16
+// value columns); the columns of H evolve independently under the rule, so a
+// single long sequence still spreads over dv / 16 workgroups per head. Per
+// chunk, wave w owns the 16-token row block w for the products over tokens
+// and the dk blocks t = w, w + 4, ... of the fp32 master state, which it keeps
+// in accumulators:
+//   X_w = K_w H and Z_w = Q_w H               (B operand: H, transposed in LDS)
+//   R_w = beta (V_w - exp(gamma) rk X_w)      -> LDS, barrier
+//   U_w = sum_{j <= w} T_wj R_j               -> LDS, barrier
+//   O_w = exp(gamma) rq Z_w + sum_{j <= w} P_wj U_j
+//   H'_t = exp(gamma_last) H_t + sum_j K_j^T (D U)_j   -> LDS, barrier
+// The K tile is staged in LDS (double-buffered) because the state advance
+// reads it transposed; every other operand of a chunk (the wave's q rows, v,
+// the T and P blocks, the scale rows) is loaded straight into registers in
+// MFMA operand layout, one chunk ahead. Workgroups of one (sequence, head)
+// are placed on one XCD so that they share its L2 for q, k, T and P.
 
 #include <hip/hip_runtime.h>
 
@@ -26,378 +39,344 @@
 #include <string>
 
 #include "gdn_internal.h"
+#include "gdn_prefill_common.h"
 
 namespace {
 
-typedef float f4 __attribute__((ext_vector_type(4)));
+using namespace gdn::pf;
 
-struct TokenParams {
-    const float* q;
-    const float* k;
-    const float* v;
-    const float* g;
-    const float* beta;
-    float* o;
-    float* pool;
-    const int32_t* cu;
-    const int32_t* src;
-    const int32_t* dst;
-    const int32_t* ckpt;        // optional [chunks] checkpoint slots
-    const int32_t* chunk_off;   // [N + 1] first chunk of each sequence (when ckpt)
-    int32_t* chunk_off_w;
-    int32_t* err;
-    int32_t hk, hv, group, num_slots, n_seqs;
-    float scale, eps;
+template <int DK>
+struct F32Tiles {
+    static_assert(DK % 16 == 0 && DK >= 16 && DK <= 128, "dk must be 16, 32, 64 or 128");
+    static constexpr int SK = DK + 4;        // LDS row stride (floats) of the K tile and of H^T
+    static constexpr int NB = DK / 16;       // 16-row blocks of dk
+    static constexpr int NT = (NB + 3) / 4;  // state blocks per wave (block t belongs to wave t % 4)
+    static constexpr int KV = DK / 16;       // float4s of the 64 x DK K tile per thread
 };
 
-// First 64-token chunk of every sequence (exclusive prefix sum of
-// ceil(len / 64)), 1024 sequences per round: a scan inside each wave, then
-// the wave totals through LDS.
-constexpr int kOffThreads = 1024;
+// Operands of one chunk as loaded from global memory (one chunk ahead).
+// Token rows are held "one row per lane": lane (row, g) = (lane % 16, lane / 16)
+// holds 4 consecutive columns 4 g .. 4 g + 3 of its row.
+template <int DK>
+struct F32Chunk {
+    f32x4 kst[F32Tiles<DK>::KV];  // K tile: float4 number tid + 256 u (row-major, DK / 4 per row) -> LDS
+    f32x4 qa[F32Tiles<DK>::NB];   // Q[16 w + row][16 b + 4 g ..]: this wave's rows, block b of dk
+    f32x4 v;                      // V[16 w + row][c0 + 4 g ..]
+    f32x4 tp[5];                  // fragments 5 w .. 5 w + 4 of the chunk's 20 T and P blocks -> LDS
+    f32x4 sc;                     // float4 number 64 w + lane of the 80 of the scale rows -> LDS
+    int ck;                       // checkpoint slot after the chunk (< 0: none)
+};
 
-__global__ void __launch_bounds__(kOffThreads) token_chunk_offsets_kernel(TokenParams p) {
-    constexpr int NWV = kOffThreads / 64;
-    __shared__ int wsum[NWV];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    int carry = 0;
-    for (int base = 0; base < p.n_seqs; base += kOffThreads) {
-        const int i = base + tid;
-        int nc = 0;
-        if (i < p.n_seqs) nc = (p.cu[i + 1] - p.cu[i] + 63) / 64;
-        int x = nc;
+// First chunk of sequence n (kernel-argument table for small calls, indexed
+// by constants only so it stays in the argument segment).
+__device__ __forceinline__ int chunk_base(const PrefillParams& p, int n) {
+    if (p.inl_n > 0) {
+        int r = 0;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(x, off);
-            if (lane >= off) x += y;
-        }
-        if (lane == 63) wsum[w] = x;
-        __syncthreads();
-        int o = carry, t = 0;
-#pragma unroll
-        for (int k = 0; k < NWV; ++k) {
-            if (k < w) o += wsum[k];
-            t += wsum[k];
-        }
-        if (i < p.n_seqs) p.chunk_off_w[i] = o + x - nc;
-        carry += t;
-        __syncthreads();                        // wsum is rewritten next round
+        for (int i = 0; i < kInlineSeqs; ++i)
+            if (i == n) r = p.inl_chunk[i];
+        return r;
     }
-    if (tid == 0) p.chunk_off_w[p.n_seqs] = carry;
+    return p.chunk_off[n];
 }
 
-// Tokens of inputs in flight: 4 for the thinnest slices (one wavefront per
-// SIMD, registers to spare; 7 % faster on one 8192-token sequence than 2),
-// 2 for wider ones, which run two wavefronts per SIMD and would lose one of
-// them to the extra registers.
-constexpr int tokens_ahead(int cols) { return cols <= 4 ? 4 : 2; }
+constexpr int kTP = 20;                    // T and P blocks of a (chunk, head) in the workspace
+constexpr int kScF4 = kScRows * kC / 4;    // float4s of its scale rows
+constexpr int kSR = kC + 4;                // LDS row stride (floats) of R, stored column-major
 
-// Lane layout of a COLS-column slice of a dk x dv tile: CG float4 column
-// groups and RG = 64 / CG row groups; lane l = rg * CG + cg holds column
-// group cg of the RPT consecutive rows rg * RPT .. rg * RPT + RPT - 1, and
-// loads those rows of k and q itself. The lanes sharing cg (a "class") hold
-// every row once, so sums over a class are sums over dk.
-template <int DK, int COLS>
-struct Slice {
-    static constexpr int CG = COLS / 4;
-    static constexpr int RG = 64 / CG;
-    static constexpr int RPT = DK / RG;   // rows per lane
-    static_assert(COLS % 4 == 0 && 64 % CG == 0 && DK % RG == 0 && RPT >= 1, "unsupported slice");
-};
+template <int DK>
+__global__ void __launch_bounds__(256) prefill_f32_recurrent_kernel(PrefillParams p, int ncg, int npairs) {
+    using S = F32Tiles<DK>;
+    constexpr int SK = S::SK, NB = S::NB, NT = S::NT, KV = S::KV;
+    // chunk operands shared by the waves, double-buffered (chunk i in buffer i % 2)
+    __shared__ __align__(16) float sK[2][64 * SK];       // K tile, row-major
+    __shared__ __align__(16) f32x4 sTP[2][kTP][64];      // T blocks 0..9, then P blocks, as fragments
+    __shared__ __align__(16) float sSc[2][kScRows * kC]; // scale rows
+    __shared__ __align__(16) float sH[16 * SK];          // H^T: sH[col * SK + dk row]
+    __shared__ __align__(16) float sR[16 * kSR];         // R^T: sR[col * kSR + token]
+    __shared__ __align__(16) f32x4 sU[4][64];            // U_w in accumulator layout
 
-template <int RPT>
-struct TokenIn {
-    float k[RPT], q[RPT];   // this lane's rows of k and q
-    f4 v;                   // this lane's column group of v
-    float g, beta;
-};
-
-template <int N>
-__device__ __forceinline__ void load_rows(const float* p, float (&x)[N]) {
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < N; i += 4) {
-            const f4 w = *reinterpret_cast<const f4*>(p + i);
-            x[i] = w.x;
-            x[i + 1] = w.y;
-            x[i + 2] = w.z;
-            x[i + 3] = w.w;
-        }
-    } else if constexpr (N == 2) {
-        const float2 w = *reinterpret_cast<const float2*>(p);
-        x[0] = w.x;
-        x[1] = w.y;
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) x[i] = p[i];
-    }
-}
-
-template <int DK, int DV, int COLS>
-__device__ __forceinline__ void fetch_token(const TokenParams& p, int t, int j, int h, int c0, int lane,
-                                            TokenIn<Slice<DK, COLS>::RPT>& in) {
-    using S = Slice<DK, COLS>;
-    const int rg = lane / S::CG, cg = lane % S::CG;
-    const size_t r = (static_cast<size_t>(t) * p.hk + j) * DK + rg * S::RPT;
-    load_rows(p.k + r, in.k);
-    load_rows(p.q + r, in.q);
-    const size_t gh = static_cast<size_t>(t) * p.hv + h;
-    in.v = *reinterpret_cast<const f4*>(p.v + gh * DV + c0 + 4 * cg);
-    in.g = p.g[gh];
-    in.beta = p.beta[gh];
-}
-
-// Cross-lane sums without LDS: DPP inside 16-lane rows, then the gfx950 row
-// and half swaps. A swap exchanges data between lane groups of its two
-// operands; with both operands equal, the sum of its two results is the sum
-// over the group pair, whichever half lands where.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float sum_row_pairs(float x) {    // lanes 16 apart
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float sum_halves(float x) {       // lanes 32 apart
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-constexpr int kQuadXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
-constexpr int kQuadXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
-constexpr int kRowRor4 = 0x124;   // rotate right by 4 inside a row
-constexpr int kRowRor8 = 0x128;   // rotate right by 8 inside a row
-
-// sum over the lanes that share lane % CG (CG in 1, 2, 4): every lane ends
-// with the sum of its class
-template <int CG>
-__device__ __forceinline__ float sum_classes(float x) {
-    if constexpr (CG == 1) x += dpp<kQuadXor1>(x);
-    if constexpr (CG <= 2) x += dpp<kQuadXor2>(x);
-    x += dpp<kRowRor4>(x);
-    x += dpp<kRowRor8>(x);
-    return sum_halves(sum_row_pairs(x));
-}
-
-template <int DK, int DV, int COLS>
-__device__ __forceinline__ void store_slice(const TokenParams& p, int slot, int h, int c0, int lane,
-                                            const f4 (&st)[Slice<DK, COLS>::RPT]) {
-    using S = Slice<DK, COLS>;
-    f4* out = reinterpret_cast<f4*>(p.pool + (static_cast<size_t>(slot) * p.hv + h) * (DK * DV) + c0);
-    const int cg = lane % S::CG, rg = lane / S::CG;
-#pragma unroll
-    for (int m = 0; m < S::RPT; ++m) out[(rg * S::RPT + m) * (DV / 4) + cg] = st[m];
-}
-
-template <int DK, int DV, int COLS>
-__global__ void __launch_bounds__(64) prefill_tokens_kernel(TokenParams p) {
-    using S = Slice<DK, COLS>;
-    static_assert(DV % COLS == 0, "unsupported tile shape");
-    constexpr int NS = DV / COLS;
-    constexpr int kAhead = tokens_ahead(COLS);
-    constexpr int CG = S::CG, RPT = S::RPT;
-    const int lane = threadIdx.x & 63;                // one wavefront per workgroup
-    const unsigned tile = blockIdx.x / NS;
-    const int c0 = static_cast<int>(blockIdx.x - tile * NS) * COLS;
-    const int n = tile / p.hv;
-    const int h = tile - n * p.hv;
-    const int cg = lane % CG, rg = lane / CG;
+    // blocks are dealt to the 8 XCDs round-robin: the ncg column groups of
+    // one (sequence, head) pair get block numbers that agree mod 8
+    const unsigned blk = blockIdx.x;
+    const int slot8 = static_cast<int>(blk >> 3);
+    const int pair = (slot8 / ncg) * 8 + static_cast<int>(blk & 7);
+    if (pair >= npairs) return;
+    const int n = pair / p.hv, h = pair - n * p.hv;
+    const int c0 = (slot8 % ncg) * 16;
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: its branches stay scalar
+    const int dv = p.dv;
 
     const int d = p.dst[n];
     if (d < 0) return;                                // sequence skipped
     const int s = p.src[n];
-    if (d >= p.num_slots || s >= p.num_slots) {
-        if (lane == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
+    const int j = h / p.group;
+    const int t0 = p.cu[n], t1 = p.cu[n + 1];
+    const int nch = (t1 - t0 + kC - 1) / kC;
+    const int cb = chunk_base(p, n);
+    // (token and chunk ranges as the host mirror of cu_seqlens promised)
+    if (d >= p.num_slots || s >= p.num_slots || t1 > p.total_tokens || t1 < t0 || cb + nch > p.num_chunks) {
+        if (tid == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
         return;
     }
-    f4 st[RPT];
-    if (s >= 0) {
-        const f4* in = reinterpret_cast<const f4*>(p.pool + (static_cast<size_t>(s) * p.hv + h) * (DK * DV) + c0);
+    const size_t tile = static_cast<size_t>(DK) * dv;
+
+    // fp32 master state: blocks t = w + 4 u of H (dk rows 16 t ..), lane
+    // (col, g) holding H[16 t + 4 g + e][c0 + col]
+    f32x4 hm[NT];
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) st[m] = in[(rg * RPT + m) * (DV / 4) + cg];
-    } else {
+    for (int u = 0; u < NT; ++u) {
+        const int t = w + 4 * u;
+        hm[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (t < NB && s >= 0) {
+            const float* in = p.pool + (static_cast<size_t>(s) * p.hv + h) * tile + c0 + l16;
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) st[m] = f4{0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < 4; ++e) hm[u][e] = in[static_cast<size_t>(16 * t + 4 * g4 + e) * dv];
+        }
     }
-
-    const int t0 = p.cu[n], t1 = p.cu[n + 1];
-    const int j = h / p.group;
-    const int cbase = p.ckpt != nullptr ? p.chunk_off[n] : 0;
-
-    // Output row of the previous token, stored only after this token's inputs
-    // have arrived: a store issued between a load and its first use would be
-    // waited for along with the load (memory operations retire in order).
-    f4 o_prev = f4{0.f, 0.f, 0.f, 0.f};
-    auto store_o = [&](int t) {
-        if (rg == 0) *reinterpret_cast<f4*>(p.o + (static_cast<size_t>(t) * p.hv + h) * DV + c0 + 4 * cg) = o_prev;
+    const auto store_state = [&](int slot) {
+        float* out = p.pool + (static_cast<size_t>(slot) * p.hv + h) * tile + c0 + l16;
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            const int t = w + 4 * u;
+            if (t < NB)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[static_cast<size_t>(16 * t + 4 * g4 + e) * dv] = hm[u][e];
+        }
+    };
+    const auto put_state_lds = [&]() {
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            const int t = w + 4 * u;
+            if (t < NB) *reinterpret_cast<f32x4*>(sH + l16 * SK + 16 * t + 4 * g4) = hm[u];
+        }
     };
 
-    // One token; `nxt` (the buffer token t - 1 used) receives the inputs of
-    // token t + kAhead - 1 while this one runs. Past the end the last token
-    // is loaded again: an unconditional load keeps the wait counts exact.
-    // H^T k and H^T q are formed on the raw k and q, beside the norms, and
-    // scaled afterwards, so the state chain does not wait for the norms.
-    auto step = [&](int t, const TokenIn<RPT>& cur, TokenIn<RPT>& nxt) {
-        const int tn = t + kAhead - 1;
-        fetch_token<DK, DV, COLS>(p, tn < t1 ? tn : t1 - 1, j, h, c0, lane, nxt);
-
-        float s_kk = 0.f, s_qq = 0.f, s_kq = 0.f;
-        f4 a = f4{0.f, 0.f, 0.f, 0.f};
-        f4 c = f4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Token rows through buffer resources spanning the chunk's valid rows:
+    // rows past the sequence end read as zero and are not stored, so no load
+    // or store needs a branch (and every wave issues the same loads, which
+    // keeps the wait counts exact).
+    const unsigned kq_row = static_cast<unsigned>(p.hk) * DK;     // floats between token rows of q and k
+    const unsigned v_row = static_cast<unsigned>(p.hv) * dv;      // ... of v and o
+    const auto kq_rsrc = [&](const float* x, int r0, int len) {
+        return make_rsrc(x + (static_cast<size_t>(r0) * p.hk + j) * DK, 4u * ((len - 1) * kq_row + DK));
+    };
+    const auto vo_rsrc = [&](const float* x, int r0, int len) {
+        return make_rsrc(x + (static_cast<size_t>(r0) * p.hv + h) * dv + c0, 4u * ((len - 1) * v_row + 16));
+    };
+    // Loads of chunk i's operands, in three parts that the chunk before it
+    // spreads over its products: a CU's vector memory unit takes each load
+    // instruction in turn, and issued all at once they would hold the waves
+    // for most of a chunk.
+    struct Rsrc {
+        rsrc_t k, q;
+    };
+    const auto chunk_rows = [&](int i) {
+        const int r0 = t0 + kC * i;
+        return Rsrc{kq_rsrc(p.kf, r0, min(kC, t1 - r0)), kq_rsrc(p.qf, r0, min(kC, t1 - r0))};
+    };
+    const auto fetch_kq = [&](const Rsrc& r, F32Chunk<DK>& in, int b) {   // K tile part b, Q rows block b
+        const unsigned q4 = tid + 256 * b, row = q4 / (DK / 4), col4 = q4 % (DK / 4);
+        in.kst[b] = buf_load_f4(r.k, 4u * (row * kq_row + 4 * col4));
+        in.qa[b] = buf_load_f4(r.q, 4u * ((16 * w + l16) * kq_row + 16 * b + 4 * g4));
+    };
+    const auto fetch_tp = [&](int i, F32Chunk<DK>& in) {
+        const size_t mat = (static_cast<size_t>(cb + i) * p.hv + h) * 2;   // T, then P (contiguous)
+        const f32x4* tpr = reinterpret_cast<const f32x4*>(p.tpf + mat * kFragFloats) + (5 * w) * 64 + lane;
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            s_kk += cur.k[m] * cur.k[m];
-            s_qq += cur.q[m] * cur.q[m];
-            s_kq += cur.k[m] * cur.q[m];
-            a += st[m] * cur.k[m];
-            c += st[m] * cur.q[m];
+        for (int u = 0; u < 5; ++u) in.tp[u] = tpr[u * 64];
+    };
+    const auto fetch_rest = [&](int i, F32Chunk<DK>& in) {
+        const int r0 = t0 + kC * i;
+        in.v = buf_load_f4(vo_rsrc(p.vf, r0, min(kC, t1 - r0)), 4u * ((16 * w + l16) * v_row + 4 * g4));
+        const rsrc_t scr = make_rsrc(p.sc + (static_cast<size_t>(cb + i) * p.hv + h) * (kScRows * kC), 16u * kScF4);
+        in.sc = buf_load_f4(scr, 16u * (64 * w + lane));
+        in.ck = p.ckpt != nullptr ? p.ckpt[cb + i] : -1;
+    };
+    const auto stage_k = [&](const F32Chunk<DK>& in, int buf, int u) {
+        const int q4 = tid + 256 * u, row = q4 / (DK / 4), col4 = q4 - row * (DK / 4);
+        *reinterpret_cast<f32x4*>(sK[buf] + row * SK + 4 * col4) = in.kst[u];
+    };
+    const auto stage_tp_sc = [&](const F32Chunk<DK>& in, int buf) {
+#pragma unroll
+        for (int u = 0; u < 5; ++u) sTP[buf][5 * w + u][lane] = in.tp[u];
+        if (64 * w + lane < kScF4) *reinterpret_cast<f32x4*>(sSc[buf] + 4 * (64 * w + lane)) = in.sc;
+    };
+
+    // One chunk; `nxt` receives the operands of chunk i + 1 meanwhile (the
+    // last chunk loads and stages its own operands again: unconditional
+    // loads keep the wait counts exact, so using `cur` never waits for them).
+    const auto chunk = [&](int i, const F32Chunk<DK>& cur, F32Chunk<DK>& nxt) {
+        const int inext = i + 1 < nch ? i + 1 : i;
+        const Rsrc rn = chunk_rows(inext);
+        const int buf = i & 1;
+        const float* kt = sK[buf];
+        const float* sc = sSc[buf];
+        const int r0 = t0 + kC * i;
+        const int len = min(kC, t1 - r0);
+        const int tr = 16 * w + l16;                  // this lane's token row (row-per-lane layouts)
+        const int f0 = w * (w + 1) / 2;               // first T block of row block w
+
+        // Every LDS operand that is ready is read in bulk ahead of the
+        // products (the scheduler would otherwise sink each read to its use
+        // and expose the LDS latency once per block).
+        f32x4 hb[NB], ka[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            hb[b] = *reinterpret_cast<const f32x4*>(sH + l16 * SK + 16 * b + 4 * g4);
+            ka[b] = *reinterpret_cast<const f32x4*>(kt + tr * SK + 16 * b + 4 * g4);
         }
-        s_kk = sum_classes<CG>(s_kk);
-        s_qq = sum_classes<CG>(s_qq);
-        s_kq = sum_classes<CG>(s_kq);
-        a.x = sum_classes<CG>(a.x);
-        a.y = sum_classes<CG>(a.y);
-        a.z = sum_classes<CG>(a.z);
-        a.w = sum_classes<CG>(a.w);
-        c.x = sum_classes<CG>(c.x);
-        c.y = sum_classes<CG>(c.y);
-        c.z = sum_classes<CG>(c.z);
-        c.w = sum_classes<CG>(c.w);
-        // hardware reciprocal square root and base-2 exponential (about
-        // 1 ulp each, far inside the fp32 accuracy bar of this path)
-        const float rk = __builtin_amdgcn_rsqf(s_kk + p.eps);
-        const float rq = p.scale * __builtin_amdgcn_rsqf(s_qq + p.eps);
-        const float kq = s_kq * rk * rq;
-        const float eg = __builtin_amdgcn_exp2f(cur.g * 1.44269504088896341f);
-        if (t > t0) store_o(t - 1);
-
-        // u = beta (v - e^g H^T k^), o = e^g H^T q~ + (k^ . q~) u, H <- e^g H + k^ u^T
-        const f4 u = cur.beta * (cur.v - (eg * rk) * a);
-        o_prev = (eg * rq) * c + kq * u;
+        // K rows as columns for the state advance: kc[u][jb][e] =
+        // K[16 jb + 4 g + e][16 t + col], t = w + 4 u
+        f32x4 kc[NT][4];
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) st[m] = eg * st[m] + (cur.k[m] * rk) * u;
-
-        if (p.ckpt != nullptr) {
-            const int r = t - t0 + 1;                  // tokens done in this sequence
-            if ((r & 63) == 0 || t + 1 == t1) {
-                const int slot = p.ckpt[cbase + (r - 1) / 64];
-                if (slot >= p.num_slots) {
-                    if (lane == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
-                } else if (slot >= 0) {
-                    store_slice<DK, DV, COLS>(p, slot, h, c0, lane, st);
-                }
+        for (int u = 0; u < NT; ++u) {
+            const int t = w + 4 * u;
+            if (t < NB) {
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) kc[u][jb][e] = kt[(16 * jb + 4 * g4 + e) * SK + 16 * t + l16];
             }
         }
-    };
+        // blocks (w, jb) of T and P, zero above the diagonal
+        f32x4 tf[4], pf[4], scd[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const f32x4 tv = sTP[buf][f0 + (jb <= w ? jb : w)][lane];
+            const f32x4 pv = sTP[buf][10 + f0 + (jb <= w ? jb : w)][lane];
+            tf[jb] = jb <= w ? tv : zero;
+            pf[jb] = jb <= w ? pv : zero;
+            scd[jb] = *reinterpret_cast<const f32x4*>(sc + kScD * kC + 16 * jb + 4 * g4);
+        }
+        const float scx = sc[kScX * kC + tr], bet = sc[kScBeta * kC + tr], scz = sc[kScZ * kC + tr];
+        const float sce = sc[kScE * kC];
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
 
-    // A ring of kAhead input buffers, indexed at compile time (no register
-    // copies between tokens).
-    if (t1 > t0) {
-        TokenIn<RPT> ring[kAhead];
+        // X_w = K_w H and Z_w = Q_w H, one row per lane (the accumulator
+        // layout of (K_w H)^T), contraction k = 16 b + 4 g + e; the next
+        // chunk's K tile and q rows are requested block by block in between
+        f32x4 x = zero, z = zero;
 #pragma unroll
-        for (int i = 0; i < kAhead - 1; ++i)
-            fetch_token<DK, DV, COLS>(p, t0 + i < t1 ? t0 + i : t1 - 1, j, h, c0, lane, ring[i]);
-        int t = t0;
-        for (; t + kAhead <= t1; t += kAhead) {
+        for (int b = 0; b < NB; ++b) {
+            x = mm16(hb[b], ka[b], x);
+            z = mm16(hb[b], cur.qa[b], z);
+            fetch_kq(rn, nxt, b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // R_w = beta (V_w - exp(gamma) rk X_w), stored transposed
+        const f32x4 rw = bet * (cur.v - scx * x);
 #pragma unroll
-            for (int i = 0; i < kAhead; ++i) step(t + i, ring[i], ring[(i + kAhead - 1) % kAhead]);
+        for (int e = 0; e < 4; ++e) sR[(4 * g4 + e) * kSR + tr] = rw[e];
+        lds_barrier();
+
+        // U_w = sum_{jb <= w} T_w,jb R_jb (accumulator layout)
+        f32x4 rr[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) rr[jb] = *reinterpret_cast<const f32x4*>(sR + l16 * kSR + 16 * jb + 4 * g4);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 uw = zero;
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) uw = mm16(tf[jb], rr[jb], uw);
+        sU[w][lane] = uw;
+        lds_barrier();
+
+        // H'_t = exp(gamma_last) H_t + sum_jb (K_jb rows as columns) (D U)_jb,
+        // interleaved with O_w = exp(gamma) rq Z_w + sum_jb P_w,jb U_jb (one
+        // row per lane: the accumulator layout of (P U)^T); in between, the
+        // next chunk's K tile goes to LDS and its T, P, v and scale rows are
+        // requested
+        f32x4 uu[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) uu[jb] = sU[jb][lane];
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 ou = scz * z;
+        f32x4 acc[NT];
+#pragma unroll
+        for (int u = 0; u < NT; ++u) acc[u] = sce * hm[u];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const f32x4 du = scd[jb] * uu[jb];
+#pragma unroll
+            for (int u = 0; u < NT; ++u)
+                if (w + 4 * u < NB) acc[u] = mm16(kc[u][jb], du, acc[u]);
+            ou = mm16(uu[jb], pf[jb], ou);
+#pragma unroll
+            for (int u = jb; u < KV; u += 4) stage_k(nxt, buf ^ 1, u);
+            if (jb == 0) fetch_tp(inext, nxt);
+            if (jb == 2) fetch_rest(inext, nxt);
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int i = 0; i < kAhead; ++i)
-            if (t + i < t1) step(t + i, ring[i], ring[(i + kAhead - 1) % kAhead]);
-        store_o(t1 - 1);
+        for (int u = 0; u < NT; ++u)
+            if (w + 4 * u < NB) hm[u] = acc[u];
+        buf_store16(__builtin_bit_cast(u32x4, ou), vo_rsrc(p.of, r0, len), 4u * (tr * v_row + 4 * g4));
+        put_state_lds();
+        {
+            const int slot = __builtin_amdgcn_readfirstlane(cur.ck);
+            if (slot >= p.num_slots) {
+                if (tid == 0 && p.err != nullptr) atomicOr(p.err, GDN_ERRFLAG_SLOT_RANGE);
+            } else if (slot >= 0) {
+                store_state(slot);
+            }
+        }
+        stage_tp_sc(nxt, buf ^ 1);
+        lds_barrier();
+    };
+
+    if (nch > 0) {
+        F32Chunk<DK> ring[2];
+        {
+            const Rsrc r = chunk_rows(0);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) fetch_kq(r, ring[0], b);
+            fetch_tp(0, ring[0]);
+            fetch_rest(0, ring[0]);
+#pragma unroll
+            for (int u = 0; u < KV; ++u) stage_k(ring[0], 0, u);
+            stage_tp_sc(ring[0], 0);
+        }
+        put_state_lds();
+        lds_barrier();
+        int i = 0;
+        for (; i + 2 <= nch; i += 2) {
+            chunk(i, ring[0], ring[1]);
+            chunk(i + 1, ring[1], ring[0]);
+        }
+        if (i < nch) chunk(i, ring[0], ring[1]);
     }
-    store_slice<DK, DV, COLS>(p, d, h, c0, lane, st);
-}
-
-int check(const char* what) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return gdn::fail(GDN_E_HIP, std::string("gdn_prefill_chunked: ") + what + " launch failed: " +
-                                        hipGetErrorString(e));
-    return GDN_OK;
-}
-
-template <int DK, int DV, int COLS>
-int launch_cols(const TokenParams& p, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(p.n_seqs) * static_cast<unsigned>(p.hv) * (DV / COLS));
-    hipLaunchKernelGGL((prefill_tokens_kernel<DK, DV, COLS>), grid, dim3(64), 0, s, p);
-    return check("fp32 token recurrence");
-}
-
-// Slice width. A wavefront's time per token is set by the instructions it
-// issues, which scale with the rows x columns it holds, so a call with few
-// (sequence, head) pairs cuts the heads into thinner slices: 16 columns
-// while that gives 2048 wavefronts (2 per SIMD), else 8, else 4. A slice
-// needs at least one row per lane group: dk * cols >= 256.
-constexpr int64_t kWaveTarget = 2048;
-
-template <int DK, int DV>
-int launch_tokens(const TokenParams& p, hipStream_t s) {
-    const int64_t pairs = static_cast<int64_t>(p.n_seqs) * p.hv;
-    if constexpr (DV >= 16 && DK * 16 >= 256)
-        if (pairs * (DV / 16) >= kWaveTarget || DK * 8 < 256) return launch_cols<DK, DV, 16>(p, s);
-    if constexpr (DK * 8 >= 256)
-        if (pairs * (DV / 8) >= kWaveTarget || DK * 4 < 256) return launch_cols<DK, DV, 8>(p, s);
-    if constexpr (DK * 4 >= 256) return launch_cols<DK, DV, 4>(p, s);
-    return launch_cols<DK, DV, 16>(p, s);
+    store_state(d);
 }
 
 template <int DK>
-int launch_dv(const TokenParams& p, int dv, hipStream_t s) {
-    switch (dv) {
-        case 16: return launch_tokens<DK, 16>(p, s);
-        case 32: return launch_tokens<DK, 32>(p, s);
-        case 64: return launch_tokens<DK, 64>(p, s);
-        case 128: return launch_tokens<DK, 128>(p, s);
-        default: return gdn::fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: unsupported dv");
-    }
+int launch_rec(const PrefillParams& p, hipStream_t s) {
+    const int ncg = p.dv / 16;
+    const int npairs = p.n_seqs * p.hv;
+    const dim3 grid(static_cast<unsigned>(8 * ncg * ((npairs + 7) / 8)));
+    hipLaunchKernelGGL((prefill_f32_recurrent_kernel<DK>), grid, dim3(256), 0, s, p, ncg, npairs);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return gdn::fail(GDN_E_HIP, std::string("gdn_prefill_chunked: fp32 recurrence launch failed: ") +
+                                        hipGetErrorString(e));
+    return GDN_OK;
 }
 
 }  // namespace
 
 namespace gdn {
+namespace pf {
 
-int launch_prefill_f32(const gdn_pool* pool, const gdn_prefill_args* a, const PrefillPlan& plan, void* workspace,
-                       void* stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    char* ws = static_cast<char*>(workspace);
-    TokenParams p;
-    p.q = static_cast<const float*>(a->q);
-    p.k = static_cast<const float*>(a->k);
-    p.v = static_cast<const float*>(a->v);
-    p.g = a->g;
-    p.beta = a->beta;
-    p.o = static_cast<float*>(a->o);
-    p.pool = pool->storage;
-    p.cu = a->cu_seqlens;
-    p.src = a->src_slots;
-    p.dst = a->dst_slots;
-    p.ckpt = a->ckpt_slots;
-    p.chunk_off = reinterpret_cast<const int32_t*>(ws + plan.off_chunk_offsets);
-    p.chunk_off_w = reinterpret_cast<int32_t*>(ws + plan.off_chunk_offsets);
-    p.err = a->err_flag;
-    p.hk = a->num_k_heads;
-    p.hv = a->num_v_heads;
-    p.group = a->num_v_heads / a->num_k_heads;
-    p.num_slots = pool->num_slots;
-    p.n_seqs = a->num_seqs;
-    p.scale = a->scale;
-    p.eps = a->l2_eps;
-    if (p.ckpt != nullptr) {
-        hipLaunchKernelGGL(token_chunk_offsets_kernel, dim3(1), dim3(kOffThreads), 0, s, p);
-        const int st = check("chunk-offset");
-        if (st != GDN_OK) return st;
-    }
-    switch (a->dk) {
-        case 16: return launch_dv<16>(p, a->dv, s);
-        case 32: return launch_dv<32>(p, a->dv, s);
-        case 64: return launch_dv<64>(p, a->dv, s);
-        case 128: return launch_dv<128>(p, a->dv, s);
+int launch_f32_recurrence(const PrefillParams& p, hipStream_t s) {
+    switch (p.dkq) {
+        case 16: return launch_rec<16>(p, s);
+        case 32: return launch_rec<32>(p, s);
+        case 64: return launch_rec<64>(p, s);
+        case 128: return launch_rec<128>(p, s);
         default: return fail(GDN_E_UNSUPPORTED, "gdn_prefill_chunked: unsupported dk");
     }
 }
 
+}  // namespace pf
 }  // namespace gdn

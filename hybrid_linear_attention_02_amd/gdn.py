@@ -587,8 +587,8 @@ def gdn_prefill_chunked(pool: StatePool, q, k, v, g, beta, o, cu_seqlens, cu_seq
                         dst_slots, *, workspace=None, scale=None, l2_eps: float = 1e-6, err_flag=None,
                         ckpt_slots=None, stream=None):
     """Varlen chunked prefill. q, k: [T, HK, dk]; v, o: [T, HV, dv], all
-    bfloat16 (chunk form on matrix cores) or all float32 (token recurrence in
-    fp32); g, beta: float32 [T, HV]; cu_seqlens: int32 device [N+1] with its host
+    bfloat16 (chunk form on bf16 matrix cores) or all float32 (the same chunk
+    form on fp32 matrix cores); g, beta: float32 [T, HV]; cu_seqlens: int32 device [N+1] with its host
     mirror; src/dst: int32 device [N]. ``workspace``: a uint8 device tensor of
     at least gdn_prefill_workspace_bytes (allocated here if None).
     ``ckpt_slots``: optional int32 device [sum ceil(len / 64)], the slot that

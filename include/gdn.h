@@ -332,9 +332,10 @@ typedef struct gdn_prefill_args {
                                      sequence, passed to the kernels by value */
     int32_t chunk_size;           /* must be 64 */
     int32_t num_k_heads, num_v_heads, dk, dv;
-    int32_t dtype;                /* GDN_DTYPE_BF16: chunked form on bf16 matrix cores, dk in
-                                     {32, 64, 128}; GDN_DTYPE_F32: the token recurrence in
-                                     fp32 (any pool head shape), for fp32 accuracy */
+    int32_t dtype;                /* GDN_DTYPE_BF16: chunked form on bf16 matrix cores;
+                                     GDN_DTYPE_F32: the same chunked form with every product
+                                     on fp32 matrix cores, for fp32 accuracy (never split
+                                     into segments); dk, dv in {16, 32, 64, 128} for both */
     const void* q;                /* [T][HK][dk] device */
     const void* k;                /* [T][HK][dk] device */
     const void* v;                /* [T][HV][dv] device */
@@ -381,8 +382,8 @@ int gdn_prefill_chunked(const gdn_pool* pool, const gdn_prefill_args* args, void
  * library routine); on its first use on a GPU it looks up that GPU's copy of
  * the array once. A call whose workspace (gdn_prefill_workspace_bytes)
  * exceeds the array returns GDN_E_INVALID and enqueues nothing: 64 MiB covers
- * one 4096-token call at 16 key / 32 value heads of 128 x 128 (52.5 MiB),
- * and every call of fp32 inputs (whose workspace holds only offsets). The workspace needs no clearing
+ * one 4096-token call at 16 key / 32 value heads of 128 x 128 in either
+ * dtype (bf16 52.5 MiB, fp32 42.5 MiB). The workspace needs no clearing
  * between calls. Every call on one GPU shares that GPU's array: two calls
  * whose work overlaps on one GPU (different streams, or graphs replayed
  * concurrently) race on it and must be serialised by the caller. The device

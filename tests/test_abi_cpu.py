@@ -369,18 +369,32 @@ def test_prefill_no_sequences_is_a_no_op(lib):
     lib.gdn_state_pool_destroy(h)
 
 
-def test_prefill_f32_accepts_every_pool_shape_and_needs_only_offsets(lib):
-    # fp32 inputs run the token recurrence: any pool head shape, and the
-    # workspace holds only the per-sequence chunk offsets
+def test_prefill_f32_workspace_holds_offsets_fp32_blocks_and_scale_rows(lib):
+    # fp32 inputs run the chunked form on the fp32 MFMA for every pool head
+    # shape, never split: the workspace holds the [N+1] chunk and segment
+    # offsets, then per (chunk, value head) T and P as ten fp32 16 x 16
+    # blocks each and five 64-float scale rows, sections in 256-byte blocks;
+    # it does not depend on dk or dv
+    up = lambda x: (x + 255) // 256 * 256
     for dk, dv in ((16, 16), (128, 128), (32, 64)):
         buf, h = _make_pool(lib, hv=2, dk=dk, dv=dv)
         _, addr = _fake_storage()
-        cuh = np.asarray([0, 64, 64, 200], np.int32)
+        cuh = np.asarray([0, 64, 64, 200], np.int32)      # 1 + 0 + 3 chunks
         a = _prefill_args(addr, cuh, dk=dk, dv=dv, dtype=gdn.GDN_DTYPE_F32)
         n = c_size_t()
         assert lib.gdn_prefill_workspace_bytes(h, byref(a), byref(n)) == gdn.GDN_OK
-        assert n.value == 512          # [N+1] chunk offsets and [N+1] segment offsets, 256-byte blocks
+        chunks, hv = 4, 2
+        assert n.value == 2 * up(4 * 4) + up(4 * chunks * hv * 2 * 10 * 256) + up(4 * chunks * hv * 5 * 64)
         lib.gdn_state_pool_destroy(h)
+    # a long fp32 sequence is not split: no segment sections
+    buf, h = _make_pool(lib, hv=2, dk=128, dv=128)
+    _, addr = _fake_storage()
+    cuh = np.asarray([0, 64 * 500], np.int32)
+    a = _prefill_args(addr, cuh, dk=128, dv=128, dtype=gdn.GDN_DTYPE_F32)
+    n = c_size_t()
+    assert lib.gdn_prefill_workspace_bytes(h, byref(a), byref(n)) == gdn.GDN_OK
+    assert n.value == 2 * 256 + 4 * 500 * 2 * (2 * 10 * 256 + 5 * 64)
+    lib.gdn_state_pool_destroy(h)
 
 
 def test_prefill_dk16_runs_on_padded_dk32_tiles(lib):

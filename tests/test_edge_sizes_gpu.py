@@ -1,6 +1,6 @@
 """GPU parity at edge sizes, through the C ABI against the fp64 oracle:
-thousands of tiny packed sequences in one prefill call (bf16 chunk form and
-fp32 token recurrence), and a 4096-request decode launch.
+thousands of tiny packed sequences in one prefill call (bf16 and fp32 chunk
+forms), and a 4096-request decode launch.
 
 Bar as elsewhere (tests/_util.py): fp32 1e-5 normwise, bf16 2e-2 max-abs on
 outputs and 1e-2 relative Frobenius on states; skipped sequences and rows

@@ -45,7 +45,7 @@ def test_prefill_bf16_head_groups(hk, hv):
 
 @pytest.mark.parametrize("hk,hv", GROUPS, ids=["G1", "G4"])
 def test_prefill_f32_head_groups(hk, hv):
-    """fp32 inputs (the token recurrence), 64 x 32 tiles."""
+    """fp32 inputs (the chunk form on fp32 matrix cores), 64 x 32 tiles."""
     lengths = [150, 1, 70]
     src = [-1, 0, 1]
     dst = [2, 3, 1]

@@ -1,5 +1,6 @@
-"""GPU parity of gdn_prefill_chunked with float32 inputs (the fp32 token
-recurrence) against the fp64 oracle, through the C ABI.
+"""GPU parity of gdn_prefill_chunked with float32 inputs (the chunk form
+with every product on fp32 matrix cores) against the fp64 oracle, through
+the C ABI.
 
 Bar (fp32 inputs): outputs of every sequence and every written state within
 1e-5 of the oracle, normwise (max |x - y| <= 1e-5 max |y|); slots that are not
@@ -157,3 +158,26 @@ def test_prefill_f32_only_empty_sequences():
     np.testing.assert_array_equal(got[2], np.zeros_like(got[2]))
     np.testing.assert_array_equal(got[3], pw.pool[0])
     np.testing.assert_array_equal(got[:2], pw.pool[:2])
+
+
+@pytest.mark.parametrize("name,lengths", [("one_seq_t8192", [8192]), ("packed_16x800", [800] * 16)])
+def test_prefill_f32_full_size_sampled_heads(name, lengths):
+    """The fp32 prefill workloads at full size, built as the benchmark builds
+    them (16 key / 32 value heads of 128 x 128, seed 2, zero initial states):
+    every head runs on the GPU; the oracle follows value heads 0, 1, 30 and
+    31 (key heads 0 and 15) through every token of every sequence."""
+    N = len(lengths)
+    src, dst = [-1] * N, list(range(N, 2 * N))
+    pw = prefill_workload(name, seed=2, lengths=lengths, HK=16, HV=32, dk=128, dv=128, dtype=F32,
+                          num_slots=2 * N)
+    og, got = _run(pw, src, dst)
+    kh, vh = [0, 15], [0, 1, 30, 31]
+    tk = pw.tokens
+    o_ref, _, fin = oracle_prefill(pw.pool[:, vh], pw.cu_seqlens, src, dst, tk.q[:, kh].astype(np.float64),
+                                   tk.k[:, kh].astype(np.float64), tk.v[:, vh].astype(np.float64),
+                                   tk.g[:, vh], tk.beta[:, vh], pw.dk ** -0.5, EPS)
+    cu = pw.cu_seqlens
+    for n in range(N):
+        a, b = cu[n], cu[n + 1]
+        check_outputs(og[a:b][:, vh], o_ref[a:b], F32, f"{name} seq {n}")
+        check_state(got[dst[n]][vh], fin[n], F32, f"{name} seq {n} slot {dst[n]}")
