@@ -577,11 +577,19 @@ def bench_prefill_f32(reps=5):
     return out
 
 
-def bench_verify(reps=50, warmup=5):
+def bench_verify(reps=48, warmup=8, layers=4):
     """Speculative-decode verification: 64 requests x 4 draft tokens at the
     16/32-head 128 x 128 bf16 shape, every draft state stored (one launch).
-    Launches are idempotent (sources are only read), so `reps` of them run
-    back to back between two events."""
+
+    HBM-only protocol: launches rotate over `layers` GDN layers, each with
+    its own 320-slot pool; between two launches of a layer the others read
+    3 x 128 MiB of sources and write 3 x 512 MiB, so the 256 MB MALL holds
+    none of a layer's sources when it runs. Launches are idempotent (sources
+    are only read), so they run back to back between two events. Reported
+    beside it: the same launches on one layer (warm: its 128 MiB of sources
+    can stay in the MALL), and a copy of the same traffic shape (torch's
+    broadcast copy of the source tiles to the 4 destinations) on the same
+    rotation."""
     import torch
     from hybrid_linear_attention_02_amd import gdn
     from hybrid_linear_attention_02_amd.workloads import spec_verify
@@ -593,47 +601,49 @@ def bench_verify(reps=50, warmup=5):
     bf = lambda x: torch.from_numpy(shp(x).view(np.int16)).view(torch.bfloat16).cuda()
     dv_ = lambda x: torch.from_numpy(shp(x)).cuda()
     q, k, v, g, b = bf(tk.q), bf(tk.k), bf(tk.v), dv_(tk.g), dv_(tk.beta)
-    storage = torch.from_numpy(wl.pool).cuda()
-    pool = gdn.gdn_state_pool_create(wl.num_slots, wl.HV, wl.dk, wl.dv, storage=storage)
+    init = torch.from_numpy(wl.pool).cuda()
+    pools = [gdn.gdn_state_pool_create(wl.num_slots, wl.HV, wl.dk, wl.dv, storage=init.clone())
+             for _ in range(layers)]
     src = torch.tensor(wl.src, dtype=torch.int32, device="cuda")
     free = np.setdiff1d(np.arange(wl.num_slots), wl.src)[:B * K]
     dst = torch.tensor(free.reshape(B, K), dtype=torch.int32, device="cuda")
     o = torch.empty_like(v)
-    call = lambda: gdn.gdn_decode_verify(pool, q, k, v, g, b, o, src, dst)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / reps * 1e-3
+
+    def timed(fn, n_layers):
+        for i in range(warmup):
+            fn(i % n_layers)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            fn(i % n_layers)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    call = lambda i: gdn.gdn_decode_verify(pools[i], q, k, v, g, b, o, src, dst)
+    t = timed(call, layers)
+    t_warm = timed(call, 1)
     per_req = verify_bytes_per_request(K, wl.HK, wl.HV, wl.dk, wl.dv, 2)
     gbs = B * per_req / t / 1e9
-    # a copy of the same shape: the 64 source tiles (128 MiB) read once and
-    # written to K destinations each (torch's broadcast copy), back to back
-    tiles = storage[src.long()].contiguous()
-    out = torch.empty((K,) + tuple(tiles.shape), dtype=torch.float32, device="cuda")
-    copy = lambda: out.copy_(tiles.unsqueeze(0).expand_as(out))
-    copy()
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        copy()
-    e1.record()
-    torch.cuda.synchronize()
-    tc = e0.elapsed_time(e1) / reps * 1e-3
-    copy_gbs = (1 + K) * tiles.numel() * 4 / tc / 1e9
-    del out, tiles
-    pool.close()
+    for pl in pools:
+        pl.close()
+    del pools
+    # a copy of the same shape on the same rotation: each layer's 64 source
+    # tiles (128 MiB) read once and written to K destinations each
+    tiles = [init[src.long()].contiguous() for _ in range(layers)]
+    outs = [torch.empty((K,) + tuple(tiles[0].shape), dtype=torch.float32, device="cuda") for _ in range(layers)]
+    copy = lambda i: outs[i].copy_(tiles[i].unsqueeze(0).expand_as(outs[i]))
+    tc = timed(copy, layers)
+    copy_gbs = (1 + K) * tiles[0].numel() * 4 / tc / 1e9
+    del outs, tiles
     return {"workload": "spec_verify_bf16_b64_k4_hk16_hv32_128x128", "value": B * K / t, "unit": "draft tok/s",
             "us_per_launch": t * 1e6, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-            "bytes_per_launch": B * per_req,
+            "bytes_per_launch": B * per_req, "layers_rotated": layers,
+            "warm_one_layer_us": t_warm * 1e6, "warm_one_layer_gbs": B * per_req / t_warm / 1e9,
             "verify_shaped_copy_gbs": copy_gbs, "vs_verify_shaped_copy": gbs / copy_gbs,
             "copy_protocol": f"the {B} source tiles x {wl.HV} heads read once and written to {K} destinations each "
-                             "(torch broadcast copy), back-to-back launches",
+                             f"(torch broadcast copy), rotating over {layers} copies",
             "vs_decode_steps": "one launch reads each source tile once for 4 tokens; 4 decode steps would move "
                                f"{4 * B * decode_bytes_per_request(wl.HK, wl.HV, wl.dk, wl.dv, 2) / 1e6:.0f} MB "
                                f"against {B * per_req / 1e6:.0f} MB"}

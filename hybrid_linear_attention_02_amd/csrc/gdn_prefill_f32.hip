@@ -27,11 +27,16 @@
 //   U_w = sum_{j <= w} T_wj R_j               -> LDS, barrier
 //   O_w = exp(gamma) rq Z_w + sum_{j <= w} P_wj U_j
 //   H'_t = exp(gamma_last) H_t + sum_j K_j^T (D U)_j   -> LDS, barrier
-// The K tile is staged in LDS (double-buffered) because the state advance
-// reads it transposed; every other operand of a chunk (the wave's q rows, v,
-// the T and P blocks, the scale rows) is loaded straight into registers in
-// MFMA operand layout, one chunk ahead. Workgroups of one (sequence, head)
-// are placed on one XCD so that they share its L2 for q, k, T and P.
+// X, Z and O are formed one row per lane (the accumulator layout of their
+// transposes), so v is loaded and o stored with one 16-byte access per lane.
+// The chunk's K tile (read transposed by the state advance), its T and P
+// blocks and its scale rows are staged in double-buffered LDS, each wave
+// loading a share; the wave's own q rows and v go straight to registers.
+// Everything is loaded one chunk ahead, the loads interleaved with the
+// products: a CU's vector memory unit takes load instructions one at a time,
+// and issued as one block they held the waves for a third of a chunk.
+// Workgroups of one (sequence, head) are placed on one XCD so that they share
+// its L2 for q, k, T and P.
 
 #include <hip/hip_runtime.h>
 
