@@ -355,7 +355,7 @@ def bench_prefill(reps=20, warmup=3):
                   "cold_ms: median of single calls, each after a 1 GiB device write",
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / BF16_PEAK_TFLOPS,
-                     "traffic": _traffic("prefill_t8192_counters.md", ["gdn_prefill.hip", "gdn_abi.cpp"],
+                     "traffic": _traffic("prefill_t8192_counters.md", ["gdn_prefill.hip", "gdn_prefill_common.h", "gdn_abi.cpp"],
                                          "hbm_bytes_per_call"),
                      "scope": "whole gdn_prefill_chunked call (prep + intra-chunk + recurrence kernels)"},
         "algorithmic_gflop": flops / 1e9,
@@ -573,6 +573,9 @@ def bench_prefill_f32(reps=5):
                      "tflops_fp32": round(tflops, 2), "frac_fp32_mfma": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4)}
         pool.close()
     out["bound"] = "mfma (fp32 16x16x4; the chunk recurrence is sequential per (sequence, head, 16 columns))"
+    out["traffic_one_seq_t8192"] = _traffic("prefill_f32_t8192_counters.md",
+                                            ["gdn_prefill.hip", "gdn_prefill_common.h", "gdn_prefill_f32.hip",
+                                             "gdn_abi.cpp"], "hbm_bytes_per_call")
     out["flops_per_token_head"] = flops_per_tok
     return out
 
@@ -1008,6 +1011,22 @@ def run_counters(launches=5, copy_mib=128):
         ws = gdn.gdn_prefill_chunked(ppool, pq, pk, pv, pg, pb, po, pcu, pw.cu_seqlens, psrc, pdst, workspace=ws)
     torch.cuda.synchronize()
     ppool.close()
+    del ws, po
+    # two calls of the fp32-input 8192-token prefill (the second one is read)
+    from hybrid_linear_attention_02_amd.workloads import F32, prefill_workload
+    fw = prefill_workload("one_seq_t8192", seed=2, lengths=[8192], HK=16, HV=32, dk=128, dv=128, dtype=F32,
+                          num_slots=2)
+    ft = fw.tokens
+    fq, fk, fv, fg, fb = dev(ft.q), dev(ft.k), dev(ft.v), dev(ft.g), dev(ft.beta)
+    fo = torch.empty_like(fv)
+    fpool = gdn.gdn_state_pool_create(2, 32, 128, 128)
+    fpool.alloc(2)
+    fcu = dev(fw.cu_seqlens)
+    ws = None
+    for _ in range(2):
+        ws = gdn.gdn_prefill_chunked(fpool, fq, fk, fv, fg, fb, fo, fcu, fw.cu_seqlens, psrc, pdst, workspace=ws)
+    torch.cuda.synchronize()
+    fpool.close()
     print(json.dumps({"decode_launches": launches,
                       "decode_algorithmic_bytes_per_launch": wl.B * decode_bytes_per_request(wl.HK, wl.HV, wl.dk, wl.dv, 2),
                       "copy_bytes_each_way": n * 4,
