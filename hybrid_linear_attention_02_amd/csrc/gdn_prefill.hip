@@ -320,23 +320,35 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
         load_gb(j * p.group, gl_next, bl_next);
         // fp32 rows in blocks of 16 features, lane (row, g) holding
         // X[row][16 b + 4 g + e]; sums of squares and the Gram tiles
-        // accumulate block by block (one block of k and q rows in flight)
+        // accumulate block by block
         float sk[4] = {0.f, 0.f, 0.f, 0.f}, sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 10; ++i) {
             gkk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             gkq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-#pragma unroll
-        for (int b = 0; b < DK / 16; ++b) {
-            f32x4 kb[4], qb[4];
+        // Rows through buffer resources over the chunk's valid rows (rows past
+        // the end read as zero), one block of 16 features in flight ahead of
+        // the products on the current one; the loop is kept rolled so the
+        // wave needs few enough registers for two waves per SIMD.
+        const unsigned kq_row = static_cast<unsigned>(p.hk) * DK;
+        const unsigned kq_bytes = 4u * ((len - 1) * kq_row + DK);
+        const rsrc_t kr = make_rsrc(p.kf + (static_cast<size_t>(t0) * p.hk + j) * DK, kq_bytes);
+        const rsrc_t qr = make_rsrc(p.qf + (static_cast<size_t>(t0) * p.hk + j) * DK, kq_bytes);
+        const auto load_block = [&](int b, f32x4* kx, f32x4* qx) {
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const int r = 16 * tt + l16;
-                const size_t off = (static_cast<size_t>(t0 + r) * p.hk + j) * DK + 16 * b + 4 * g4;
-                kb[tt] = r < len ? *reinterpret_cast<const f32x4*>(p.kf + off) : f32x4{0.f, 0.f, 0.f, 0.f};
-                qb[tt] = r < len ? *reinterpret_cast<const f32x4*>(p.qf + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+                const unsigned off = 4u * ((16 * tt + l16) * kq_row + 16 * b + 4 * g4);
+                kx[tt] = buf_load_f4(kr, off);
+                qx[tt] = buf_load_f4(qr, off);
             }
+        };
+        f32x4 kb[4], qb[4];
+        load_block(0, kb, qb);
+#pragma unroll 1
+        for (int b = 0; b < DK / 16; ++b) {
+            f32x4 kn[4], qn[4];
+            load_block(b + 1 < DK / 16 ? b + 1 : b, kn, qn);   // (the last block loads itself again)
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
@@ -352,6 +364,11 @@ __global__ void __launch_bounds__(64) prefill_intra_kernel(PrefillParams p) {
                     gkk[ix] = mm16(kb[ts], kb[tr], gkk[ix]);
                     gkq[ix] = mm16(kb[ts], qb[tr], gkq[ix]);
                 }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                kb[tt] = kn[tt];
+                qb[tt] = qn[tt];
+            }
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
