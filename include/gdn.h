@@ -354,7 +354,10 @@ typedef struct gdn_prefill_args {
 } gdn_prefill_args;
 
 /* Bytes of device workspace gdn_prefill_chunked needs for these args (depends
- * on N, the chunk count from cu_seqlens_host, and the head shape). */
+ * on N, the chunk count from cu_seqlens_host, the head shape and the dtype:
+ * per (chunk, value head) the T and P matrices, 16 KiB in bf16 or 20 KiB as
+ * fp32 blocks, and 1.25 KiB of scale rows; plus, for bf16 calls the planner
+ * splits, per-segment end states and transitions). */
 int gdn_prefill_workspace_bytes(const gdn_pool* pool, const gdn_prefill_args* args, size_t* bytes);
 
 /* Run every sequence through the rule from its source state and write the
