@@ -68,6 +68,14 @@ def prefill_flops_per_token(HV, dk, dv, C=64, G=2):
     return HV * (2 * C * dk + 4 * C * dv + 6 * dk * dv + 4 * C * dk // G)
 
 
+def prefill_f32_flops_per_token_head(dk, dv, C=64, G=2):
+    """Algorithmic flops per token and value head of the fp32 chunk form:
+    K H, Q H and the state advance (6 dk dv), the triangular T R and P U
+    (2 (C + 1) dv), the triangular Gram matrices shared by the G value heads
+    of a key head (2 C dk / G) and the triangular solve (C^2 / 3)."""
+    return 6 * dk * dv + 2 * (C + 1) * dv + 2 * C * dk / G + C * C / 3
+
+
 def prefill_bytes_per_token(HK, HV, dk, dv, elem=2):
     return 2 * HK * dk * elem + 2 * HV * dv * elem + 8 * HV
 
@@ -542,8 +550,7 @@ def bench_prefill_f32(reps=5):
     from hybrid_linear_attention_02_amd import gdn
     from hybrid_linear_attention_02_amd.workloads import F32, prefill_workload
 
-    C, G, dk, dv = 64, 2, 128, 128
-    flops_per_tok = 6 * dk * dv + 2 * (C + 1) * dv + 2 * C * dk / G + C * C / 3
+    flops_per_tok = prefill_f32_flops_per_token_head(128, 128)
     out = {}
     for name, lengths in (("one_seq_t8192", [8192]), ("packed_16x800", [800] * 16)):
         pw = prefill_workload(name, seed=2, lengths=lengths, HK=16, HV=32, dk=128, dv=128, dtype=F32,

@@ -43,6 +43,17 @@ def test_prefill_flops_and_bytes_per_token_by_hand():
     assert bench.prefill_bytes_per_token(16, 32, 128, 128) == 24_832
 
 
+def test_prefill_f32_flops_per_token_by_hand():
+    # per token and value head at 128 x 128, C = 64, G = 2: K H, Q H and the
+    # state advance 3 x 2 x 128 x 128; T R and P U over the lower triangle
+    # including the diagonal, (64 + 1) / 2 tokens on average, 2 x 2 x 32.5 x 128;
+    # K K^T and Q K^T over their lower triangles, 64 x 128 per token per key
+    # head, halved over the two value heads; the solve 64^3 / 3 per chunk
+    want = 3 * 2 * 128 * 128 + 2 * 2 * 32.5 * 128 + 2 * 64 * 128 / 2 + 64 ** 3 / 3 / 64
+    assert bench.prefill_f32_flops_per_token_head(128, 128) == pytest.approx(want)
+    assert want == pytest.approx(124_501.33, abs=0.01)
+
+
 def test_traffic_lookup_follows_the_kernel_source(tmp_path, monkeypatch):
     csrc = tmp_path / "hybrid_linear_attention_02_amd" / "csrc"
     csrc.mkdir(parents=True)
@@ -61,7 +72,8 @@ def test_traffic_lookup_follows_the_kernel_source(tmp_path, monkeypatch):
 
 def test_committed_counter_summaries_carry_their_keys():
     for name, key in (("decode_counters_batched_b64_h32_128x128.txt", "hbm_bytes_per_launch"),
-                      ("prefill_t8192_counters.md", "hbm_bytes_per_call")):
+                      ("prefill_t8192_counters.md", "hbm_bytes_per_call"),
+                      ("prefill_f32_t8192_counters.md", "hbm_bytes_per_call")):
         path = os.path.join(ROOT, "profiles", name)
         text = open(path).read()
         assert "kernel_source_sha256_16:" in text
