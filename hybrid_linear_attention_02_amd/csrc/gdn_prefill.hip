@@ -37,6 +37,12 @@
 //
 // Raw (unnormalised) bf16 q and k are the MFMA operands; the L2 norms and the
 // decay factors are applied as fp32 row scales on the accumulator side.
+//
+// float32 inputs use the same intra-chunk kernel instantiated for fp32 rows
+// (Gram products on the fp32 MFMA, T and P written as fp32 blocks) and the
+// fp32 recurrence of gdn_prefill_f32.hip; the parameter block, the sequence
+// lookup and the small helpers both files share are in
+// gdn_prefill_common.h.
 
 #include <hip/hip_runtime.h>
 #include <type_traits>
